@@ -1,0 +1,154 @@
+/*
+ * msr.h -- C ABI of libmsr.so: multi-scale retention (MSR) on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by site and section):
+ *   - Q is rotated by Theta and K by its conjugate with the rotate-every-two
+ *     cos/sin shift (jsqmd.com "From RoPE to Retention", section 2, the
+ *     theta_shift snippet).  Pair i = (x[2i], x[2i+1]) of a token at absolute
+ *     position p becomes (x0 cos a - x1 sin a, x1 cos a + x0 sin a) with
+ *     a = p * theta[i].  The same real rotation is applied to Q and K: their
+ *     real dot product then depends only on the position difference, which
+ *     is what the conjugate pairing provides.
+ *   - Scores are scaled by d_k^-0.5 (same page, section 5).  The scale is
+ *     folded into the rotated K, so the carried state holds scaled keys.
+ *   - Decay mask D[n][m] = gamma_h^(n-m) for n >= m, else 0, one gamma per
+ *     head (same page, section 3; aiqz.cc RetNet tutorial, "retention score
+ *     and exponential decay", "multi-scale retention").
+ *   - Three equivalent forms (jsqmd.com section 4; aiqz.cc "parallel",
+ *     "recurrent" and "chunkwise" representations; b99b.cn QbitAI article):
+ *       parallel   O = (Q~ K~^T (.) D) V  (+ gamma^(n+1) Q~ S_in)
+ *       chunkwise  per chunk i of b tokens, local index j, token t:
+ *                  O = (Q~_i K~_i^T (.) D_b) V_i + (Q~_i S_{i-1}) (.) xi,
+ *                  xi_j = gamma^(j+1);
+ *                  S_i = gamma^b S_{i-1} + K~_i^T (V_i (.) zeta),
+ *                  zeta_t = gamma^(b-1-t)
+ *       recurrent  S_n = gamma S_{n-1} + k~_n^T v_n ;  o_n = q~_n S_n
+ *   - Each head's output row (d_v values of one token) goes through a
+ *     GroupNorm with no affine: (x - mean) / sqrt(biased var + eps)
+ *     (jsqmd.com section 5; b99b.cn, GroupNorm's scale invariance).
+ *
+ * Layouts (row-major, no padding):
+ *   Q, K   [B][T][H][dk]      dtype of the problem (fp32 or bf16)
+ *   V, O   [B][T][H][dv]      dtype of the problem
+ *   state  [B][H][dk][dv]     always fp32
+ *   For msr_recurrent_step T is 1: q, k are [B][H][dk], v, o are [B][H][dv].
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers; gamma and theta are HOST arrays
+ *     read during the call.  The caller owns every buffer; the library keeps
+ *     no pointer after it returns and allocates no device memory.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  Buffers must stay
+ *     valid until the stream has passed the call.
+ *   - All validation happens before anything is launched; on a non-OK status
+ *     nothing has been written.  msr_last_error() then describes the
+ *     problem.  A failed launch returns MSR_ERR_HIP.  Device faults surface
+ *     at the caller's next synchronisation.
+ *   - Device pointers must be 16-byte aligned.  O must not overlap Q, K, V
+ *     or the state; state_out may equal state_in.
+ *   - Non-finite input values are not checked; they propagate.
+ *   - Scratch memory only ever comes from the caller's workspace `ws`, sized
+ *     by msr_workspace_size().  Calls that share a workspace must be ordered
+ *     on one stream.
+ *   - The library is stateless apart from the per-thread error text, so calls
+ *     from several host threads are safe when their buffers are distinct.
+ */
+#ifndef MSR_H
+#define MSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSR_ABI_VERSION 1
+#define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
+#define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
+#define MSR_MAX_DV 1024   /* d_v limit */
+
+typedef enum {
+    MSR_OK = 0,
+    MSR_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad parameter value */
+    MSR_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes, b not dividing T */
+    MSR_ERR_DTYPE = -3,       /* unknown dtype */
+    MSR_ERR_UNSUPPORTED = -4, /* valid problem this build does not handle */
+    MSR_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    MSR_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+} msr_status;
+
+typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
+
+/* flags: switch parts of the operation off (used for staged checks) */
+enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u };
+
+/* forms, for msr_workspace_size */
+enum { MSR_FORM_PARALLEL = 0, MSR_FORM_CHUNKWISE = 1, MSR_FORM_STEP = 2 };
+
+typedef struct {
+    int32_t B, T, H, dk, dv; /* dk even, 2..MSR_MAX_DK; dv 4..MSR_MAX_DV, multiple of 4 */
+    int32_t dtype;           /* msr_dtype of Q, K, V, O */
+    const float *gamma;      /* [host] H decays, each in (0, 1] */
+    const float *theta;      /* [host] dk/2 frequencies, or NULL => 10000^(-2i/dk) */
+    float scale;             /* 0 => dk^-0.5; multiplies the rotated K */
+    float gn_eps;            /* GroupNorm epsilon, >= 0 (1e-5 is the usual value) */
+    int64_t pos0;            /* absolute position of token 0 (>= 0) for the rotation */
+    uint32_t flags;          /* MSR_FLAG_* */
+} msr_problem;
+
+/* Library version check: returns MSR_ABI_VERSION. */
+int msr_abi_version(void);
+
+/* Text describing the last non-OK status returned on this host thread. */
+const char *msr_last_error(void);
+
+/*
+ * Workspace bytes needed by `form` (MSR_FORM_*) for problem p; `chunk` is
+ * the chunk size b for MSR_FORM_CHUNKWISE and ignored otherwise.  Validates
+ * p like the compute calls (pointer fields are not dereferenced except
+ * gamma/theta) and writes *bytes only on MSR_OK.
+ */
+msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
+                              size_t *bytes);
+
+/*
+ * Parallel form over all T tokens of every (batch, head) pair
+ * (jsqmd.com section 4.1; aiqz.cc "parallel representation"):
+ *   O[n] = GN( sum_{m<=n} gamma^(n-m) (q~_n . k~_m) v_m + gamma^(n+1) q~_n S_in )
+ *   state_out = gamma^T S_in + sum_m gamma^(T-1-m) k~_m^T v_m
+ * state_in NULL means a zero incoming state; state_out NULL skips it.
+ * Equal, up to rounding, to msr_chunkwise with chunk == T.
+ */
+msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, const void *V,
+                        void *O, const float *state_in, float *state_out, void *ws,
+                        size_t ws_bytes, void *hip_stream);
+
+/*
+ * Chunkwise-recurrent form with chunk size `chunk` (1 <= chunk, chunk divides
+ * T, else MSR_ERR_SHAPE) (jsqmd.com section 4.3; aiqz.cc "chunkwise
+ * recurrence"): the intra-chunk parallel product plus the decayed state
+ * carried across chunks, as in the header comment.  Same outputs and state
+ * as msr_parallel up to rounding.
+ */
+msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
+                         const void *V, void *O, const float *state_in, float *state_out,
+                         void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * One recurrent decode step for every pair, p->T must be 1 and p->pos0 is
+ * the absolute position of the token (jsqmd.com section 4.2; aiqz.cc
+ * "recurrent representation"):
+ *   state <- gamma state + k~^T v   (in place, fp32)
+ *   o      = GN(q~ state)           (uses the updated state)
+ * Needs no workspace.
+ */
+msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k,
+                              const void *v, void *o, float *state, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSR_H */

@@ -1,0 +1,58 @@
+"""Build libmsr.so (HIP for gfx950) in-tree with hipcc.
+
+Usage: python -m retnet_scale_retention_amd.build
+Every source is compiled for gfx950 only; objects go to _build/, the shared
+library to retnet_scale_retention_amd/libmsr.so.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+OUT = PKG / "libmsr.so"
+BUILD = PKG / "_build"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# packed-fp32 instructions are disabled for all device code
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+          f"-I{ROOT / 'include'}", f"-I{CSRC}"]
+
+
+def sources():
+    return sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
+
+
+def _compile(src: Path) -> Path:
+    obj = BUILD / (src.name + ".o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", str(src), "-o", str(obj)]
+    if src.suffix == ".cpp":
+        cmd = [HIPCC, *COMMON, "-c", str(src), "-o", str(obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src.name}:\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int = 8) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = OUT.with_suffix(".so.tmp")
+    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(int(sys.argv[1]) if len(sys.argv) > 1 else 8))

@@ -1,0 +1,51 @@
+// msr_internal.hpp -- shared between the C-ABI layer (msr_api.cpp) and the
+// HIP kernels: the per-call constant block and the launcher prototypes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msr.h"
+
+// Per-call constants, passed BY VALUE as a kernel argument (about 2 KiB, far
+// below the kernel-argument limit), so no host->device copy is ever needed.
+struct MsrConst {
+    int32_t B, T, H, dk, dv;
+    int32_t chunk;     // chunk size b (T for the parallel form)
+    int64_t pos0;      // absolute position of token 0
+    float scale;       // multiplies the rotated K
+    float eps;         // GroupNorm epsilon
+    uint32_t flags;    // MSR_FLAG_*
+    int32_t pad_;
+    float gamma[MSR_MAX_HEADS];   // decay per head
+    float log2g[MSR_MAX_HEADS];   // log2(gamma), computed in fp64 on the host
+    float theta[MSR_MAX_DK / 2];  // rotation frequency per channel pair
+};
+
+// ---- launchers (defined in the .hip files); all enqueue on `st` ----------
+
+// X [B][T][H][dk] (fp32 or bf16) -> Xr [B][H][T][dk] fp32, rotated at
+// positions pos0 + t and multiplied by `factor`.
+hipError_t launch_rotate(const MsrConst &c, int dtype, const void *X, float *Xr, float factor,
+                         hipStream_t st);
+
+// Generic state pass over chunks of size `chunk`:
+//   chunk_states[pair][i] = state entering chunk i (optional),
+//   s_out = state after the last chunk (optional).
+hipError_t launch_generic_state(const MsrConst &c, int dtype, int chunk, const float *Kr,
+                                const void *V, const float *s_in, float *s_out,
+                                float *chunk_states, hipStream_t st);
+
+// Generic output pass: intra-chunk product + cross-chunk term read from
+// states + pair * pair_stride + chunk_index * chunk_stride (states may be
+// NULL: no cross-chunk term), GroupNorm, store O.
+hipError_t launch_generic_output(const MsrConst &c, int dtype, int chunk, const float *Qr,
+                                 const float *Kr, const void *V, void *O, const float *states,
+                                 int64_t pair_stride, int64_t chunk_stride, hipStream_t st);
+
+// Recurrent decode step, state updated in place.
+hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void *k,
+                         const void *v, void *o, float *state, hipStream_t st);
+
+// s_out = s_in (or zeros when s_in is NULL); used for T == 0.
+hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out, hipStream_t st);

@@ -1,0 +1,115 @@
+"""CPU-only checks of the C ABI: the library loads, exports what
+include/msr.h declares, and rejects invalid calls before touching a GPU."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import retnet_scale_retention_amd as msr
+from retnet_scale_retention_amd import msr as m
+
+ROOT = Path(__file__).resolve().parents[1]
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation
+
+
+def header_functions():
+    text = (ROOT / "include" / "msr.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = msr.load()
+    names = header_functions()
+    assert set(names) == set(m.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.msr_abi_version() == 1
+
+
+def desc(**kw):
+    base = dict(B=2, T=64, H=4, dk=16, dv=32, dtype=m.MSR_BF16, gamma=np.full(4, 0.9))
+    base.update(kw)
+    return m._Desc(**base)
+
+
+def status_ws(d, form=m.MSR_FORM_CHUNKWISE, chunk=16):
+    n = ctypes.c_size_t(12345)
+    s = msr.load().msr_workspace_size(d.ref, form, chunk, ctypes.byref(n))
+    return s, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=15), m.STATUS.get(-2)), (dict(dk=0), "MSR_ERR_SHAPE"), (dict(dk=1024), "MSR_ERR_SHAPE"),
+    (dict(dv=6), "MSR_ERR_SHAPE"), (dict(dv=2048), "MSR_ERR_SHAPE"), (dict(H=0, gamma=np.zeros(0)), "MSR_ERR_SHAPE"),
+    (dict(B=-1), "MSR_ERR_SHAPE"), (dict(dtype=7), "MSR_ERR_DTYPE"),
+    (dict(gamma=np.array([0.9, 0.9, 0.9, 1.5])), "MSR_ERR_INVALID_ARG"),
+    (dict(gamma=np.array([0.9, 0.0, 0.9, 0.9])), "MSR_ERR_INVALID_ARG"),
+    (dict(gamma=np.array([0.9, np.nan, 0.9, 0.9])), "MSR_ERR_INVALID_ARG"),
+    (dict(eps=-1.0), "MSR_ERR_INVALID_ARG"), (dict(pos0=-3), "MSR_ERR_INVALID_ARG"),
+    (dict(flags=8), "MSR_ERR_INVALID_ARG"), (dict(scale=float("inf")), "MSR_ERR_INVALID_ARG"),
+])
+def test_invalid_problems_are_rejected(kw, code):
+    s, n = status_ws(desc(**kw))
+    assert m.STATUS[s] == code
+    assert n == 12345  # untouched on error
+    assert msr.load().msr_last_error().decode()
+
+
+def test_chunk_must_divide_T():
+    d = desc(T=96)
+    assert status_ws(d, chunk=32)[0] == 0
+    assert m.STATUS[status_ws(d, chunk=40)[0]] == "MSR_ERR_SHAPE"
+    assert m.STATUS[status_ws(d, chunk=0)[0]] == "MSR_ERR_SHAPE"
+
+
+def test_workspace_sizes_are_stable_and_step_needs_none():
+    d = desc()
+    s1, n1 = status_ws(d, m.MSR_FORM_CHUNKWISE, 16)
+    s2, n2 = status_ws(d, m.MSR_FORM_PARALLEL, 0)
+    assert s1 == 0 and s2 == 0 and n1 > 0 and n2 > 0
+    s3, n3 = status_ws(desc(T=1), m.MSR_FORM_STEP, 0)
+    assert s3 == 0 and n3 == 0
+    assert m.STATUS[status_ws(desc(T=4), m.MSR_FORM_STEP, 0)[0]] == "MSR_ERR_SHAPE"
+
+
+def test_calls_validate_pointers_before_any_launch():
+    lib = msr.load()
+    d = desc()
+    null = ctypes.c_void_p()
+    # missing tensors
+    s = lib.msr_parallel(d.ref, null, FAKE, FAKE, FAKE, null, null, FAKE, 1 << 40, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    # misaligned tensor
+    s = lib.msr_chunkwise(d.ref, 16, ctypes.c_void_p(0x10002), FAKE, FAKE, ctypes.c_void_p(0x20000),
+                          null, null, FAKE, 1 << 40, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    # O aliasing Q
+    s = lib.msr_chunkwise(d.ref, 16, FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), FAKE,
+                          null, null, FAKE, 1 << 40, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    # workspace too small / missing
+    O = ctypes.c_void_p(0x40000)
+    s = lib.msr_chunkwise(d.ref, 16, FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), O,
+                          null, null, FAKE, 16, null)
+    assert m.STATUS[s] == "MSR_ERR_WORKSPACE"
+    s = lib.msr_parallel(d.ref, FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), O,
+                         null, null, null, 0, null)
+    assert m.STATUS[s] == "MSR_ERR_WORKSPACE"
+    # decode step: T must be 1, o must not alias the state
+    s = lib.msr_recurrent_step(desc(T=2).ref, FAKE, FAKE, FAKE, O, FAKE, null)
+    assert m.STATUS[s] == "MSR_ERR_SHAPE"
+    s = lib.msr_recurrent_step(desc(T=1).ref, FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000),
+                               O, O, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    assert "alias" in lib.msr_last_error().decode()
+
+
+def test_null_problem_and_bytes():
+    lib = msr.load()
+    n = ctypes.c_size_t(0)
+    assert m.STATUS[lib.msr_workspace_size(None, 1, 16, ctypes.byref(n))] == "MSR_ERR_INVALID_ARG"
+    assert m.STATUS[lib.msr_workspace_size(desc().ref, 1, 16, None)] == "MSR_ERR_INVALID_ARG"
+    assert m.STATUS[lib.msr_workspace_size(desc().ref, 9, 16, ctypes.byref(n))] == "MSR_ERR_INVALID_ARG"
