@@ -69,44 +69,33 @@ __device__ __forceinline__ bf16x8 ld_lds8(const __bf16 *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// 8 bf16 from global memory at p (16-byte aligned), rotated pairwise with
-// the 4 (cos, sin) entries at cs: (x0 c - x1 s, x1 c + x0 s).
-__device__ __forceinline__ bf16x8 load_rot8(const uint16_t *p, const float2 *cs, bool rotate) {
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(p);
-    bf16x8 out;
-    if (rotate) {
-        const float4 c01 = *reinterpret_cast<const float4 *>(cs);
-        const float4 c23 = *reinterpret_cast<const float4 *>(cs + 2);
-        const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
-        const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = __uint_as_float(raw[i] << 16);
-            const float x1 = __uint_as_float(raw[i] & 0xffff0000u);
-            out[2 * i] = static_cast<__bf16>(x0 * cc[i] - x1 * ss[i]);
-            out[2 * i + 1] = static_cast<__bf16>(x1 * cc[i] + x0 * ss[i]);
-        }
-    } else {
-        out = __builtin_bit_cast(bf16x8, raw);
-    }
-    return out;
-}
-
 template <int DK, int BC>
 struct Cfg {
-    static constexpr int NW = (BC / 16 < 8 ? BC / 16 : 8) < DK / 16 ? (BC / 16 < 8 ? BC / 16 : 8) : DK / 16;
+    static constexpr int NKT = BC / 16;                  // 16-token tiles per chunk
+    static constexpr int NW = NKT < 8 ? NKT : 8;         // waves
+    static constexpr int NQT = NKT / NW;                 // query tiles per wave (1 or 2)
     static constexpr int THREADS = NW * 64;
-    static constexpr int QB = 16 * NW;      // query rows per block
-    static constexpr int NQB = BC / QB;     // query blocks per chunk
-    static constexpr int RS = DK / NW;      // state rows per wave
-    static constexpr int RT = RS / 16;      // state row tiles per wave
-    static constexpr int CT = W / 16;       // column tiles
+    static constexpr int CT = W / 16;          // state / output column tiles
+    static constexpr int NT = (DK / 16) * CT;  // state tiles per workgroup
+    static constexpr int TPW = NT / NW;        // state tiles per wave
+    static constexpr int CPW = TPW < CT ? TPW : CT;  // ... of which column tiles
+    static constexpr int RPW = TPW / CPW;            // ... and row tiles
+    static constexpr int CG = CT / CPW;              // column groups of waves
     static constexpr int KS = DK / 32;      // k-steps over d_k
-    static constexpr int KP = DK + 8;       // padded LDS row (bf16) of K~
+    static constexpr int XP = DK + 8;       // padded LDS row (bf16) of Q~ / K~
     static constexpr int VP = W + 8;        // padded LDS row of V
     static constexpr int SP = DK + 8;       // padded LDS row of S^T
-    static constexpr size_t LDS_BYTES =
-        (size_t)BC * KP * 2 + (size_t)BC * VP * 2 + (size_t)W * SP * 2 + 3 * BC * 4;
+    static constexpr int PAIRS8 = DK / 8;   // 8-element pieces per Q/K row
+    static constexpr int ITER = BC * PAIRS8 / THREADS;  // Q/K pieces per thread per chunk
+    static constexpr int TSTRIDE = THREADS / PAIRS8;    // token stride between them
+    static constexpr int VITER = BC * (W / 8) / THREADS;
+    static constexpr size_t LDS_BYTES = (size_t)BC * XP * 2 + 2 * (size_t)BC * VP * 2 +
+                                        (size_t)W * SP * 2 + 2 * BC * 4;
+    static_assert(NKT % NW == 0 && NQT <= 2, "query tiles split over waves");
+    static_assert(NT % NW == 0 && TPW >= 1, "state tiles must split evenly over waves");
+    static_assert(BC * PAIRS8 % THREADS == 0 && THREADS % PAIRS8 == 0, "staging split");
+    static_assert(BC * (W / 8) % THREADS == 0, "V staging split");
+    static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
 
 struct ChunkArgs {
@@ -119,21 +108,43 @@ struct ChunkArgs {
     int NS;            // slices per pair (dv / W)
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Rotate 4 channel pairs (8 bf16 packed in u) by the angles with cos/sin
+// (cc[i], ss[i]): (x0 c - x1 s, x1 c + x0 s) in fp32, rounded to bf16.
+__device__ __forceinline__ u32x4 rot4(u32x4 u, const float *cc, const float *ss) {
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x0 = __uint_as_float(u[i] << 16);
+        const float x1 = __uint_as_float(u[i] & 0xffff0000u);
+        const bf16x2 y = {static_cast<__bf16>(x0 * cc[i] - x1 * ss[i]),
+                          static_cast<__bf16>(x1 * cc[i] + x0 * ss[i])};
+        out[i] = __builtin_bit_cast(uint32_t, y);
+    }
+    return out;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2 y = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, y);
+}
+
 template <int DK, int BC>
 __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    __bf16 *Ks = reinterpret_cast<__bf16 *>(smem);                   // [BC][KP]
-    __bf16 *Vs = Ks + BC * C::KP;                                      // [BC][VP]
-    __bf16 *St = Vs + BC * C::VP;                                      // [W][SP]
-    float *dec = reinterpret_cast<float *>(St + W * C::SP);            // scale gamma^d
-    float *zet = dec + BC;                                             // scale gamma^(BC-1-t)
-    float *xi = zet + BC;                                              // gamma^(j+1)
+    __bf16 *Xs = reinterpret_cast<__bf16 *>(smem);                   // [BC][XP]  Q~, then K~
+    __bf16 *Vs = Xs + BC * C::XP;                                      // [BC][VP]  V
+    __bf16 *Vz = Vs + BC * C::VP;                                      // [BC][VP]  V zeta s
+    __bf16 *St = Vz + BC * C::VP;                                      // [W][SP]   S_old^T
+    float *dec = reinterpret_cast<float *>(St + W * C::SP);            // s gamma^d
+    float *xi = dec + BC;                                              // gamma^(j+1)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
-    // workgroup -> (pair, slice); consecutive ids run on different XCDs, so
-    // the slices of one pair are placed on the same XCD (id % 8 equal).
+    // workgroup -> (pair, slice): the slices of one pair get ids equal mod 8,
+    // i.e. run on the same XCD and share its L2 for the Q and K chunks.
     const int npairs = c.B * c.H;
     int pair, slice;
     {
@@ -156,112 +167,231 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 
     for (int t = tid; t < BC; t += C::THREADS) {
         dec[t] = c.scale * exp2f((float)t * lg);
-        zet[t] = c.scale * exp2f((float)(BC - 1 - t) * lg);
         xi[t] = exp2f((float)(t + 1) * lg);
     }
     const float gb = exp2f((float)BC * lg);
 
-    // ---- state slice in accumulators: rows w*RS + rt*16 + 4g + r, col ct*16 + l16
-    f32x4 S[C::RT][C::CT];
+    // ---- staging assignment: this thread owns channel pairs p0..p0+3 of
+    // tokens tf, tf + TSTRIDE, ... of every chunk (same pairs for Q and K).
+    const int tf = tid / C::PAIRS8;
+    const int d0 = (tid % C::PAIRS8) * 8;
+    float stc[4], sts[4];  // cos/sin of TSTRIDE * theta for the 4 pairs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rot_cos_sin(C::TSTRIDE, c.theta[d0 / 2 + i], stc[i], sts[i]);
+    const int vt0 = tid / (W / 8), vd0 = (tid % (W / 8)) * 8;
+    constexpr int VSTRIDE = C::THREADS / (W / 8);
+
+    // zeta s for this thread's V tokens (same in every chunk)
+    float zv[C::VITER];
+#pragma unroll
+    for (int it = 0; it < C::VITER; ++it)
+        zv[it] = c.scale * exp2f((float)(BC - 1 - (vt0 + it * VSTRIDE)) * lg);
+
+    u32x4 rq[C::ITER], rk[C::ITER], rv[C::VITER];
+    float2 cs0[4];
+    // raw Q (issued late, after the MFMA work of a chunk) and raw K, V and
+    // the first cos/sin (issued right after staging) of the next chunk
+    auto prefetch_q = [&](int t0) {
+        const size_t tok = (size_t)b * c.T + t0 + tf;
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it)
+            rq[it] = *reinterpret_cast<const u32x4 *>(a.q + (tok + (size_t)it * C::TSTRIDE) * rowQK +
+                                                      (size_t)h * DK + d0);
+    };
+    auto prefetch_kv = [&](int t0) {
+        const size_t tok = (size_t)b * c.T + t0 + tf;
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it)
+            rk[it] = *reinterpret_cast<const u32x4 *>(a.k + (tok + (size_t)it * C::TSTRIDE) * rowQK +
+                                                      (size_t)h * DK + d0);
+        const size_t tokv = (size_t)b * c.T + t0 + vt0;
+#pragma unroll
+        for (int it = 0; it < C::VITER; ++it)
+            rv[it] = *reinterpret_cast<const u32x4 *>(
+                a.v + (tokv + (size_t)it * VSTRIDE) * rowV + (size_t)h * c.dv + col0 + vd0);
+        const float4 *cp = reinterpret_cast<const float4 *>(a.cs + (size_t)(t0 + tf) * (DK / 2) + d0 / 2);
+        const float4 c01 = cp[0], c23 = cp[1];
+        cs0[0] = make_float2(c01.x, c01.y);
+        cs0[1] = make_float2(c01.z, c01.w);
+        cs0[2] = make_float2(c23.x, c23.y);
+        cs0[3] = make_float2(c23.z, c23.w);
+    };
+
+    // ---- state tiles of this wave: rows (rg*RPW + rt)*16 + 4g + r, cols (cg*CPW + ct)*16 + l16
+    const int cgw = w % C::CG, rgw = w / C::CG;
+    f32x4 S[C::RPW][C::CPW];
     const size_t sbase = (size_t)pair * DK * c.dv + col0;
 #pragma unroll
-    for (int rt = 0; rt < C::RT; ++rt)
+    for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct)
+        for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = w * C::RS + rt * 16 + 4 * g + r;
-                S[rt][ct][r] = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + ct * 16 + l16] : 0.f;
+                const int row = (rgw * C::RPW + rt) * 16 + 4 * g + r;
+                const int col = (cgw * C::CPW + ct) * 16 + l16;
+                S[rt][ct][r] = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
             }
     auto write_st = [&]() {
 #pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt)
+        for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                __bf16 *dst = St + (ct * 16 + l16) * C::SP + w * C::RS + rt * 16 + 4 * g;
+            for (int ct = 0; ct < C::CPW; ++ct) {
+                const int row = (rgw * C::RPW + rt) * 16 + 4 * g;
+                const int col = (cgw * C::CPW + ct) * 16 + l16;
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 bf16x4 v4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v4[r] = static_cast<__bf16>(S[rt][ct][r]);
-                *reinterpret_cast<bf16x4 *>(dst) = v4;
+                *reinterpret_cast<bf16x4 *>(St + col * C::SP + row) = v4;
             }
     };
+
+    prefetch_q(0);
+    prefetch_kv(0);
     write_st();
 
     const int nchunks = c.T / BC;
+    // query tiles of this wave: w and, when there are two, NKT-1-w (balances
+    // the causal work between waves)
+    int qtile[C::NQT];
+    qtile[0] = w;
+    if (C::NQT == 2) qtile[C::NQT - 1] = C::NKT - 1 - w;
     for (int ci = 0; ci < nchunks; ++ci) {
         const int t0 = ci * BC;
-        __syncthreads();  // previous chunk finished with Ks, Vs; St written
-        // ---- stage K~ (rotated, unscaled) and the V slice
-        for (int e = tid; e < BC * (DK / 8); e += C::THREADS) {
-            const int t = e / (DK / 8), d0 = (e % (DK / 8)) * 8;
-            const uint16_t *src = a.k + ((size_t)b * c.T + t0 + t) * rowQK + (size_t)h * DK + d0;
-            const float2 *cs = a.cs + (size_t)(t0 + t) * (DK / 2) + d0 / 2;
-            *reinterpret_cast<bf16x8 *>(Ks + t * C::KP + d0) = load_rot8(src, cs, rotate);
-        }
-        for (int e = tid; e < BC * (W / 8); e += C::THREADS) {
-            const int t = e / (W / 8), d0 = (e % (W / 8)) * 8;
-            const uint16_t *src = a.v + ((size_t)b * c.T + t0 + t) * rowV + (size_t)h * c.dv + col0 + d0;
-            *reinterpret_cast<u32x4 *>(Vs + t * C::VP + d0) = *reinterpret_cast<const u32x4 *>(src);
-        }
-        __syncthreads();
-
-        // ---- queries of this wave: O^T = S_old^T Q~^T xi + V^T P^T
-        for (int qb = 0; qb < C::NQB; ++qb) {
-            const int j0 = qb * C::QB + 16 * w;  // first query row (within chunk) of this wave
-            const int jq = j0 + l16;             // this lane's query column
-            bf16x8 qreg[C::KS];
-            {
-                const size_t tq = (size_t)t0 + jq;
-                const uint16_t *src = a.q + ((size_t)b * c.T + tq) * rowQK + (size_t)h * DK + 8 * g;
-                const float2 *cs = a.cs + tq * (DK / 2) + 4 * g;
+        // ---- rotate Q and K pieces (cos/sin advanced by TSTRIDE per piece)
+        if (rotate) {
+            float cc[4], ss[4];
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = load_rot8(src + 32 * ks, cs + 16 * ks, rotate);
+            for (int i = 0; i < 4; ++i) {
+                cc[i] = cs0[i].x;
+                ss[i] = cs0[i].y;
             }
+#pragma unroll
+            for (int it = 0; it < C::ITER; ++it) {
+                rq[it] = rot4(rq[it], cc, ss);
+                rk[it] = rot4(rk[it], cc, ss);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float nc = cc[i] * stc[i] - ss[i] * sts[i];
+                    const float ns = ss[i] * stc[i] + cc[i] * sts[i];
+                    cc[i] = nc;
+                    ss[i] = ns;
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it)
+            *reinterpret_cast<u32x4 *>(Xs + (tf + it * C::TSTRIDE) * C::XP + d0) = rq[it];
+        __syncthreads();  // Q~ staged; St holds S_old
+        bf16x8 qreg[C::NQT][C::KS];
+#pragma unroll
+        for (int u = 0; u < C::NQT; ++u)
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                qreg[u][ks] = ld_lds8(Xs + (16 * qtile[u] + l16) * C::XP + 32 * ks + 8 * g);
+        __syncthreads();  // every wave has its Q~ rows
+#pragma unroll
+        for (int it = 0; it < C::ITER; ++it)
+            *reinterpret_cast<u32x4 *>(Xs + (tf + it * C::TSTRIDE) * C::XP + d0) = rk[it];
+#pragma unroll
+        for (int it = 0; it < C::VITER; ++it) {
+            const int t = vt0 + it * VSTRIDE;
+            *reinterpret_cast<u32x4 *>(Vs + t * C::VP + vd0) = rv[it];
+            u32x4 z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                z[i] = pack_bf16x2(__uint_as_float(rv[it][i] << 16) * zv[it],
+                                   __uint_as_float(rv[it][i] & 0xffff0000u) * zv[it]);
+            *reinterpret_cast<u32x4 *>(Vz + t * C::VP + vd0) = z;
+        }
+        if (ci + 1 < nchunks) prefetch_kv(t0 + BC);  // next chunk's loads fly during the compute
+        __syncthreads();  // K~, V, V zeta staged
+
+        // ---- state update S = gamma^b S + K~^T (V zeta s) on this wave's tiles
+#pragma unroll
+        for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
+#pragma unroll 2
+        for (int s = 0; s < BC / 32; ++s) {
+            const int tb = 32 * s + 8 * g;  // first token of this lane group
+            bf16x8 bv[C::CPW];
+#pragma unroll
+            for (int ct = 0; ct < C::CPW; ++ct) {
+                const __bf16 *base = Vz + (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
+                bv[ct] = cat(lds_tr(base + (tb + (l16 >> 2)) * C::VP),
+                             lds_tr(base + (tb + 4 + (l16 >> 2)) * C::VP));
+            }
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt) {
+                const __bf16 *base = Xs + (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
+                const bf16x8 ak = cat(lds_tr(base + (tb + (l16 >> 2)) * C::XP),
+                                      lds_tr(base + (tb + 4 + (l16 >> 2)) * C::XP));
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
+            }
+        }
+
+#pragma unroll
+        for (int u = 0; u < C::NQT; ++u) {
+            const int qt = qtile[u];
+            const int jq = 16 * qt + l16;  // this lane's query row within the chunk
+            // ---- O^T = (S_old^T Q~^T) xi   (four independent accumulators)
             f32x4 oacc[C::CT];
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks)
-                    acc = mfma16(ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g), qreg[ks], acc);
+            for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct)
+                    oacc[ct] = mfma16(ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g), qreg[u][ks],
+                                      oacc[ct]);
+            {
                 const float x = xi[jq];
-                oacc[ct] = acc * x;
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * x;
             }
-            // intra-chunk keys 0 .. j0+15, in steps of 32
-            const int nsteps = (j0 + 16 + 31) / 32;
-            for (int s = 0; s < nsteps; ++s) {
-                f32x4 p[2];
+            // ---- intra-chunk part, keys 0 .. 16qt+15, four key tiles at a time:
+            // P^T tiles (decay, scale and causal mask in registers) packed as
+            // B operands, then O^T += V^T P^T
+#pragma unroll 1
+            for (int kq = 0; kq < C::NKT; kq += 4) {
+                if (kq <= qt) {
+                    f32x4 acc[4];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int kt0 = 32 * s + 16 * half;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (kt0 <= j0 + 15) {
+                    for (int v4 = 0; v4 < 4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int ks = 0; ks < C::KS; ++ks)
-                            acc = mfma16(ld_lds8(Ks + (kt0 + l16) * C::KP + 32 * ks + 8 * g), qreg[ks], acc);
+                    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+                        for (int v4 = 0; v4 < 4; ++v4)
+                            if (kq + v4 <= qt)
+                                acc[v4] = mfma16(ld_lds8(Xs + (16 * (kq + v4) + l16) * C::XP + 32 * ks + 8 * g),
+                                                 qreg[u][ks], acc[v4]);
+                    bf16x8 pb[2];
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = 16 * (kq + v4) + 4 * g + r;
+                            const float x = (t <= jq) ? acc[v4][r] * dec[jq - t] : 0.f;
+                            pb[v4 / 2][4 * (v4 & 1) + r] = static_cast<__bf16>(x);
+                        }
+#pragma unroll
+                    for (int hs = 0; hs < 2; ++hs) {
+                        const int s = kq / 2 + hs;
+                        if (2 * s <= qt) {
+#pragma unroll
+                            for (int ct = 0; ct < C::CT; ++ct) {
+                                const __bf16 *base = Vs + ct * 16 + 4 * (l16 & 3);
+                                const s16x4 lo = lds_tr(base + (32 * s + 4 * g + (l16 >> 2)) * C::VP);
+                                const s16x4 hi = lds_tr(base + (32 * s + 16 + 4 * g + (l16 >> 2)) * C::VP);
+                                oacc[ct] = mfma16(cat(lo, hi), pb[hs], oacc[ct]);
+                            }
+                        }
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = kt0 + 4 * g + r;
-                        acc[r] = (t <= jq) ? acc[r] * dec[jq - t] : 0.f;
-                    }
-                    p[half] = acc;
-                }
-                bf16x8 pb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pb[r] = static_cast<__bf16>(p[0][r]);
-                    pb[4 + r] = static_cast<__bf16>(p[1][r]);
-                }
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) {
-                    const __bf16 *base = Vs + ct * 16 + 4 * (l16 & 3);
-                    const s16x4 lo = lds_tr(base + (32 * s + 4 * g + (l16 >> 2)) * C::VP);
-                    const s16x4 hi = lds_tr(base + (32 * s + 16 + 4 * g + (l16 >> 2)) * C::VP);
-                    oacc[ct] = mfma16(cat(lo, hi), pb, oacc[ct]);
                 }
             }
+            if (u == C::NQT - 1 && ci + 1 < nchunks) prefetch_q(t0 + BC);
             // ---- GroupNorm over the row (lanes l16, l16+16, +32, +48 share a query)
             const size_t orow = ((size_t)b * c.T + t0 + jq) * c.H + h;
             float sum = 0.f;
@@ -295,49 +425,20 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 *reinterpret_cast<bf16x4 *>(dst + ct * 16) = v4;
             }
         }
-
-        // ---- state update S = gamma^b S + K~^T (V zeta s), rows of this wave
-#pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) S[rt][ct] = S[rt][ct] * gb;
-        for (int s = 0; s < BC / 32; ++s) {
-            bf16x8 bv[C::CT];
-            const int tb = 32 * s + 8 * g;  // first token of this lane group
-#pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                const __bf16 *base = Vs + ct * 16 + 4 * (l16 & 3);
-                const s16x4 lo = lds_tr(base + (tb + (l16 >> 2)) * C::VP);
-                const s16x4 hi = lds_tr(base + (tb + 4 + (l16 >> 2)) * C::VP);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bv[ct][e] = static_cast<__bf16>(bf(lo[e]) * zet[tb + e]);
-                    bv[ct][4 + e] = static_cast<__bf16>(bf(hi[e]) * zet[tb + 4 + e]);
-                }
-            }
-#pragma unroll
-            for (int rt = 0; rt < C::RT; ++rt) {
-                const __bf16 *base = Ks + w * C::RS + rt * 16 + 4 * (l16 & 3);
-                const s16x4 lo = lds_tr(base + (tb + (l16 >> 2)) * C::KP);
-                const s16x4 hi = lds_tr(base + (tb + 4 + (l16 >> 2)) * C::KP);
-                const bf16x8 ak = cat(lo, hi);
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
-            }
-        }
-        __syncthreads();  // every wave is done reading St (old state)
+        __syncthreads();  // every wave is done with Xs, Vs, Vz and St
         write_st();
     }
 
     if (a.s_out) {
 #pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt)
+        for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct)
+            for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = w * C::RS + rt * 16 + 4 * g + r;
-                    a.s_out[sbase + (size_t)row * c.dv + ct * 16 + l16] = S[rt][ct][r];
+                    const int row = (rgw * C::RPW + rt) * 16 + 4 * g + r;
+                    const int col = (cgw * C::CPW + ct) * 16 + l16;
+                    a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r];
                 }
     }
 }
@@ -356,24 +457,39 @@ __global__ void angle_table_kernel(MsrConst c, float2 *cs) {
 }
 
 // GroupNorm of rows whose slices wrote (mean, M2) statistics: combines the
-// NS slice statistics (Chan et al.'s pairwise update) and normalises the
-// d_v values of the row in place.  One wave per row.
-__global__ void gn_finalize_kernel(MsrConst c, int NS, const float2 *stats, uint16_t *o, size_t rows) {
-    const int lane = threadIdx.x & 63;
-    const size_t row = blockIdx.x * (size_t)(blockDim.x / 64) + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    float n = 0.f, mean = 0.f, m2 = 0.f;
-    for (int s = 0; s < NS; ++s) {
-        const float2 st = stats[row * NS + s];
-        const float nb = (float)W, nn = n + nb;
-        const float d = st.x - mean;
-        mean += d * (nb / nn);
-        m2 += st.y + d * d * (n * nb / nn);
-        n = nn;
+// NS slice statistics (Chan, Golub and LeVeque's pairwise update) once per
+// row, then normalises the row's d_v values in place, 8 values (16 bytes)
+// per thread.  A block of 256 threads covers RB = 256 / (d_v / 8) rows.
+__global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, const float2 *stats,
+                                                          uint16_t *o, size_t rows) {
+    __shared__ float2 mi[256];
+    const int tpr = c.dv / 8;          // threads per row
+    const int RB = 256 / tpr;          // rows per block
+    const size_t row0 = blockIdx.x * (size_t)RB;
+    if (threadIdx.x < RB && row0 + threadIdx.x < rows) {
+        const size_t row = row0 + threadIdx.x;
+        float n = 0.f, mean = 0.f, m2 = 0.f;
+        for (int s = 0; s < NS; ++s) {
+            const float2 st = stats[row * NS + s];
+            const float nb = (float)W, nn = n + nb;
+            const float d = st.x - mean;
+            mean += d * (nb / nn);
+            m2 += st.y + d * d * (n * nb / nn);
+            n = nn;
+        }
+        mi[threadIdx.x] = make_float2(mean, 1.f / sqrtf(m2 / n + c.eps));
     }
-    const float inv = 1.f / sqrtf(m2 / n + c.eps);
-    uint16_t *p = o + row * c.dv;
-    for (int j = lane; j < c.dv; j += 64) p[j] = f32_to_bf16((bf16_to_f32(p[j]) - mean) * inv);
+    __syncthreads();
+    const int r = threadIdx.x / tpr, j = threadIdx.x % tpr;
+    if (r >= RB || row0 + r >= rows) return;
+    const float mean = mi[r].x, inv = mi[r].y;
+    u32x4 *p = reinterpret_cast<u32x4 *>(o + (row0 + r) * c.dv) + j;
+    u32x4 u = *p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        u[i] = pack_bf16x2((__uint_as_float(u[i] << 16) - mean) * inv,
+                           (__uint_as_float(u[i] & 0xffff0000u) - mean) * inv);
+    *p = u;
 }
 
 template <int DK, int BC>
@@ -463,7 +579,8 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     if (e != hipSuccess) return e;
     if (a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;
-        const size_t blocks = (rows + 3) / 4;
+        const int RB = 256 / (p->dv / 8);
+        const size_t blocks = (rows + RB - 1) / RB;
         hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, a.NS,
                            a.stats, a.o, rows);
         e = hipGetLastError();

@@ -12,7 +12,9 @@ from pathlib import Path
 
 import numpy as np
 
-LIB_PATH = Path(__file__).resolve().parent / "libmsr.so"
+import os
+
+LIB_PATH = Path(os.environ.get("MSR_LIB", Path(__file__).resolve().parent / "libmsr.so"))
 
 MSR_OK = 0
 MSR_F32, MSR_BF16 = 0, 1
