@@ -5,16 +5,25 @@
 //   O_i = GN( (Q~_i K~_i^T (.) D) V_i + (Q~_i S_{i-1}) (.) xi )
 //   S_i = gamma^b S_{i-1} + K~_i^T (V_i (.) zeta)
 //
-// Work decomposition.  One workgroup owns one (batch, head) pair and one
-// slice of W = 64 value columns for the WHOLE sequence; its fp32 state slice
-// S[dk][W] lives in MFMA accumulators for the entire run, split over the
-// waves by rows of d_k.  Per chunk the workgroup
-//   1. stages the chunk's rotated K~ [b][dk] and its V slice [b][W] in LDS
-//      (bf16), the rotation read from a per-call cos/sin table;
+// Kernels, in launch order:
+//   angle_table_kernel  cos/sin of (pos0 + t) theta_i for every position
+//   rotate_qk_kernel    Q~, K~ = theta_shift(Q), theta_shift(K) as bf16, once
+//                       per token and head (bandwidth bound)
+//   chunk_mfma_kernel   the chunk recurrence, below
+//   gn_finalize_kernel  GroupNorm when d_v spans several slices
+//
+// Work decomposition of chunk_mfma_kernel.  One workgroup owns one (batch,
+// head) pair and one slice of W = 64 value columns for the WHOLE sequence;
+// its fp32 state slice S[dk][W] lives in MFMA accumulators for the entire
+// run, split over the waves in 16x16 tiles.  Per chunk the workgroup
+//   1. stages the chunk's K~ [b][dk], its V slice [b][W] and V (.) zeta s in
+//      LDS (bf16); each wave holds the Q~ rows of its query tiles in registers
+//      (loaded straight from memory in MFMA operand layout); all of it was
+//      prefetched into registers during the previous chunk;
 //   2. state update: S = gamma^b S + K~^T (V (.) zeta s) -- both operands are
 //      token-contiguous reads of the row-major LDS tiles, done with the gfx950
 //      LDS transpose read (ds_read_b64_tr_b16);
-//   3. for its 16 query rows each wave keeps Q~ in registers and computes
+//   3. per query tile of 16 rows:
 //        O^T  = (S_old^T Q~^T) (.) xi                 (S_old^T bf16 in LDS)
 //        P^T  = mask(K~ Q~^T) -- decay and scale applied in registers
 //        O^T += V^T P^T      -- P^T stays in registers: two 16x16 result
@@ -23,7 +32,7 @@
 //                              {4g..4g+3, 16+4g..16+4g+3} for lane group g,
 //                              and V^T is read in that same order;
 //      then GroupNorm over d_v (in-wave when W == d_v, else the slice writes
-//      its row statistics and a small finalize pass normalises);
+//      its row statistics and the finalize pass normalises);
 //   4. writes S_new^T as bf16 to LDS for the next chunk's inter-chunk term.
 // Decay factors gamma^d are exp2(d log2 gamma) with d >= 0, tabulated once
 // per workgroup in LDS.
@@ -71,8 +80,10 @@ __device__ __forceinline__ bf16x8 ld_lds8(const __bf16 *p) {
 
 template <int DK, int BC>
 struct Cfg {
+    static constexpr int KB = 64;                        // keys per LDS block
+    static constexpr int NB = BC / KB;                   // key blocks per chunk
     static constexpr int NKT = BC / 16;                  // 16-token tiles per chunk
-    static constexpr int NW = NKT < 8 ? NKT : 8;         // waves
+    static constexpr int NW = NKT >= 4 ? NKT / 2 : NKT;  // waves (two query tiles each)
     static constexpr int NQT = NKT / NW;                 // query tiles per wave (1 or 2)
     static constexpr int THREADS = NW * 64;
     static constexpr int CT = W / 16;          // state / output column tiles
@@ -82,69 +93,81 @@ struct Cfg {
     static constexpr int RPW = TPW / CPW;            // ... and row tiles
     static constexpr int CG = CT / CPW;              // column groups of waves
     static constexpr int KS = DK / 32;      // k-steps over d_k
-    static constexpr int XP = DK + 8;       // padded LDS row (bf16) of Q~ / K~
-    static constexpr int VP = W + 8;        // padded LDS row of V
-    static constexpr int SP = DK + 8;       // padded LDS row of S^T
-    static constexpr int PAIRS8 = DK / 8;   // 8-element pieces per Q/K row
-    static constexpr int ITER = BC * PAIRS8 / THREADS;  // Q/K pieces per thread per chunk
-    static constexpr int TSTRIDE = THREADS / PAIRS8;    // token stride between them
-    static constexpr int VITER = BC * (W / 8) / THREADS;
-    static constexpr size_t LDS_BYTES = (size_t)BC * XP * 2 + 2 * (size_t)BC * VP * 2 +
-                                        (size_t)W * SP * 2 + 2 * BC * 4;
+    static constexpr int KROW = DK * 2;     // bytes per K~ row in LDS (unpadded, swizzled)
+    static constexpr int KBLK = KB * KROW;  // bytes per K~ block
+    static constexpr int VROW = W * 2;      // bytes per V row
+    static constexpr int VBLK = KB * VROW;  // bytes per V block
+    static constexpr int KUPW = KBLK / 1024 / NW;  // 1 KiB direct loads per wave per K~ block
+    static constexpr int VUPW = VBLK / 1024 / NW;  // ... per V block
+    static constexpr int SP = DK + 8;       // padded LDS row of S^T (bf16)
+    static constexpr size_t LDS_BYTES = 2 * (size_t)KBLK + 2 * (size_t)VBLK + (size_t)W * SP * 2 + 3 * BC * 4;
     static_assert(NKT % NW == 0 && NQT <= 2, "query tiles split over waves");
     static_assert(NT % NW == 0 && TPW >= 1, "state tiles must split evenly over waves");
-    static_assert(BC * PAIRS8 % THREADS == 0 && THREADS % PAIRS8 == 0, "staging split");
-    static_assert(BC * (W / 8) % THREADS == 0, "V staging split");
+    static_assert(KUPW >= 1 && KUPW * NW * 1024 == KBLK, "K~ block loads");
+    static_assert(VUPW >= 1 && VUPW * NW * 1024 == VBLK, "V block loads");
     static_assert(LDS_BYTES <= 163840, "LDS budget");
+    // XOR swizzle of the 16-byte chunks of a row: 16 consecutive rows read
+    // at one logical chunk hit 16 different bank groups
+    __device__ static int swz_k(int row) { return DK >= 128 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static int swz_v(int row) { return (row >> 1) & 7; }
+    __device__ static int koff(int row, int col) {  // byte offset of K~[row][col] in a block
+        return row * KROW + ((((col >> 3) ^ swz_k(row))) << 4) + (col & 7) * 2;
+    }
+    __device__ static int voff(int row, int col) {
+        return row * VROW + ((((col >> 3) ^ swz_v(row))) << 4) + (col & 7) * 2;
+    }
 };
 
 struct ChunkArgs {
-    const uint16_t *q, *k, *v;
+    const uint16_t *q, *k, *v;  // Q~, K~ (already rotated), V
     uint16_t *o;
     const float *s_in;
     float *s_out;
-    const float2 *cs;  // [T][dk/2] cos/sin of (pos0 + t) theta_i
-    float2 *stats;     // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
-    int NS;            // slices per pair (dv / W)
+    float2 *stats;  // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
+    int NS;         // slices per pair (dv / W)
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Rotate 4 channel pairs (8 bf16 packed in u) by the angles with cos/sin
-// (cc[i], ss[i]): (x0 c - x1 s, x1 c + x0 s) in fp32, rounded to bf16.
-__device__ __forceinline__ u32x4 rot4(u32x4 u, const float *cc, const float *ss) {
-    u32x4 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x0 = __uint_as_float(u[i] << 16);
-        const float x1 = __uint_as_float(u[i] & 0xffff0000u);
-        const bf16x2 y = {static_cast<__bf16>(x0 * cc[i] - x1 * ss[i]),
-                          static_cast<__bf16>(x1 * cc[i] + x0 * ss[i])};
-        out[i] = __builtin_bit_cast(uint32_t, y);
-    }
-    return out;
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     const bf16x2 y = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
     return __builtin_bit_cast(uint32_t, y);
 }
 
+__device__ __forceinline__ u32x4 ld16(const char *base, uint32_t off) {
+    return *reinterpret_cast<const u32x4 *>(base + off);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (the LDS address is wave-uniform).
+__device__ __forceinline__ void load_lds16(const void *gptr, void *lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gptr,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Keeps the scheduler from moving instructions across this point: used to
+// issue the LDS fragment loads of the next k-step before the MFMAs of the
+// current one.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ s16x4 lds_tr_b(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
+}
+
 template <int DK, int BC>
 __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    __bf16 *Xs = reinterpret_cast<__bf16 *>(smem);                   // [BC][XP]  Q~, then K~
-    __bf16 *Vs = Xs + BC * C::XP;                                      // [BC][VP]  V
-    __bf16 *Vz = Vs + BC * C::VP;                                      // [BC][VP]  V zeta s
-    __bf16 *St = Vz + BC * C::VP;                                      // [W][SP]   S_old^T
-    float *dec = reinterpret_cast<float *>(St + W * C::SP);            // s gamma^d
-    float *xi = dec + BC;                                              // gamma^(j+1)
+    // two separate K~/V buffers (distinct LDS objects, so the compiler can
+    // tell that the direct loads into one do not alias reads of the other)
+    __shared__ __attribute__((aligned(16))) char Kb0[C::KBLK], Kb1[C::KBLK];
+    __shared__ __attribute__((aligned(16))) char Vb0[C::VBLK], Vb1[C::VBLK];
+    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_old^T
+    __shared__ float dec[BC], xi[BC], zet[BC];  // s gamma^d, gamma^(j+1), s gamma^(BC-1-t)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     // workgroup -> (pair, slice): the slices of one pair get ids equal mod 8,
-    // i.e. run on the same XCD and share its L2 for the Q and K chunks.
+    // i.e. run on the same XCD and share its L2 for the Q~ and K~ chunks.
     const int npairs = c.B * c.H;
     int pair, slice;
     {
@@ -161,60 +184,51 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * W;
     const float lg = c.log2g[h];
-    const bool rotate = !(c.flags & MSR_FLAG_NO_ROTATE);
-    const size_t rowQK = (size_t)c.H * DK;  // elements between tokens in Q, K
-    const size_t rowV = (size_t)c.H * c.dv;
 
     for (int t = tid; t < BC; t += C::THREADS) {
         dec[t] = c.scale * exp2f((float)t * lg);
         xi[t] = exp2f((float)(t + 1) * lg);
+        zet[t] = c.scale * exp2f((float)(BC - 1 - t) * lg);
     }
     const float gb = exp2f((float)BC * lg);
 
-    // ---- staging assignment: this thread owns channel pairs p0..p0+3 of
-    // tokens tf, tf + TSTRIDE, ... of every chunk (same pairs for Q and K).
-    const int tf = tid / C::PAIRS8;
-    const int d0 = (tid % C::PAIRS8) * 8;
-    float stc[4], sts[4];  // cos/sin of TSTRIDE * theta for the 4 pairs
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rot_cos_sin(C::TSTRIDE, c.theta[d0 / 2 + i], stc[i], sts[i]);
-    const int vt0 = tid / (W / 8), vd0 = (tid % (W / 8)) * 8;
-    constexpr int VSTRIDE = C::THREADS / (W / 8);
+    // uniform bases of this pair's rows; per-thread byte offsets fit 32 bits
+    const uint32_t rowQK = (uint32_t)c.H * DK * 2;        // bytes between tokens of Q~, K~
+    const uint32_t rowV = (uint32_t)c.H * c.dv * 2;       // bytes between tokens of V
+    const char *qb = reinterpret_cast<const char *>(a.q + ((size_t)b * c.T * c.H + h) * DK);
+    const char *kb = reinterpret_cast<const char *>(a.k + ((size_t)b * c.T * c.H + h) * DK);
+    const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
 
-    // zeta s for this thread's V tokens (same in every chunk)
-    float zv[C::VITER];
+    // direct loads of key block `blk` (global index over the sequence) into buffer `buf`
+    auto load_block = [&](int blk, char *Kd, char *Vd) {
+        const int tok0 = blk * C::KB;
 #pragma unroll
-    for (int it = 0; it < C::VITER; ++it)
-        zv[it] = c.scale * exp2f((float)(BC - 1 - (vt0 + it * VSTRIDE)) * lg);
-
-    u32x4 rq[C::ITER], rk[C::ITER], rv[C::VITER];
-    float2 cs0[4];
-    // raw Q (issued late, after the MFMA work of a chunk) and raw K, V and
-    // the first cos/sin (issued right after staging) of the next chunk
-    auto prefetch_q = [&](int t0) {
-        const size_t tok = (size_t)b * c.T + t0 + tf;
+        for (int i = 0; i < C::KUPW; ++i) {
+            const int byte = (w * C::KUPW + i) * 1024 + lane * 16;  // position in the block
+            const int row = byte / C::KROW, phys = (byte % C::KROW) >> 4;
+            const int chunk = phys ^ C::swz_k(row);
+            load_lds16(kb + (uint32_t)(tok0 + row) * rowQK + chunk * 16, Kd + (w * C::KUPW + i) * 1024);
+        }
 #pragma unroll
-        for (int it = 0; it < C::ITER; ++it)
-            rq[it] = *reinterpret_cast<const u32x4 *>(a.q + (tok + (size_t)it * C::TSTRIDE) * rowQK +
-                                                      (size_t)h * DK + d0);
+        for (int i = 0; i < C::VUPW; ++i) {
+            const int byte = (w * C::VUPW + i) * 1024 + lane * 16;
+            const int row = byte / C::VROW, phys = (byte % C::VROW) >> 4;
+            const int chunk = phys ^ C::swz_v(row);
+            load_lds16(vb + (uint32_t)(tok0 + row) * rowV + chunk * 16, Vd + (w * C::VUPW + i) * 1024);
+        }
     };
-    auto prefetch_kv = [&](int t0) {
-        const size_t tok = (size_t)b * c.T + t0 + tf;
+
+    // query tiles of this wave: w and, when there are two, NKT-1-w
+    int qtile[C::NQT];
+    qtile[0] = w;
+    if (C::NQT == 2) qtile[C::NQT - 1] = C::NKT - 1 - w;
+    u32x4 qn[C::NQT][C::KS];  // next chunk's Q~ rows, MFMA operand layout
+    auto prefetch_q = [&](int t0) {
 #pragma unroll
-        for (int it = 0; it < C::ITER; ++it)
-            rk[it] = *reinterpret_cast<const u32x4 *>(a.k + (tok + (size_t)it * C::TSTRIDE) * rowQK +
-                                                      (size_t)h * DK + d0);
-        const size_t tokv = (size_t)b * c.T + t0 + vt0;
+        for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-        for (int it = 0; it < C::VITER; ++it)
-            rv[it] = *reinterpret_cast<const u32x4 *>(
-                a.v + (tokv + (size_t)it * VSTRIDE) * rowV + (size_t)h * c.dv + col0 + vd0);
-        const float4 *cp = reinterpret_cast<const float4 *>(a.cs + (size_t)(t0 + tf) * (DK / 2) + d0 / 2);
-        const float4 c01 = cp[0], c23 = cp[1];
-        cs0[0] = make_float2(c01.x, c01.y);
-        cs0[1] = make_float2(c01.z, c01.w);
-        cs0[2] = make_float2(c23.x, c23.y);
-        cs0[3] = make_float2(c23.z, c23.w);
+            for (int ks = 0; ks < C::KS; ++ks)
+                qn[u][ks] = ld16(qb, (uint32_t)(t0 + 16 * qtile[u] + l16) * rowQK + (32 * ks + 8 * g) * 2);
     };
 
     // ---- state tiles of this wave: rows (rg*RPW + rt)*16 + 4g + r, cols (cg*CPW + ct)*16 + l16
@@ -246,188 +260,229 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             }
     };
 
-    prefetch_q(0);
-    prefetch_kv(0);
-    write_st();
+    // finished, not yet stored outputs of the previous chunk
+    uint32_t pend_o[C::NQT][C::CT][2];
+    size_t pend_row[C::NQT];
+    float2 pend_stat[C::NQT];
+    const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    auto flush = [&]() {
+#pragma unroll
+        for (int u = 0; u < C::NQT; ++u) {
+            uint16_t *dst = a.o + pend_row[u] * c.dv + col0 + 4 * g;
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct) {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
+                *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+            }
+            if (stats_out && g == 0) a.stats[pend_row[u] * a.NS + slice] = pend_stat[u];
+        }
+    };
 
     const int nchunks = c.T / BC;
-    // query tiles of this wave: w and, when there are two, NKT-1-w (balances
-    // the causal work between waves)
-    int qtile[C::NQT];
-    qtile[0] = w;
-    if (C::NQT == 2) qtile[C::NQT - 1] = C::NKT - 1 - w;
-    for (int ci = 0; ci < nchunks; ++ci) {
+    const int nblocks = nchunks * C::NB;
+    if (nblocks > 0) {
+        load_block(0, Kb0, Vb0);
+        prefetch_q(0);
+    }
+    write_st();
+
+    bf16x8 qreg[C::NQT][C::KS];
+    f32x4 oacc[C::NQT][C::CT];
+    // one key block: compute on (Kc, Vc) while the next block streams into (Kn, Vn)
+    auto step = [&](int blk, const char *Kc, const char *Vc, char *Kn, char *Vn) {
+        const int ci = blk / C::NB, kbi = blk % C::NB;
         const int t0 = ci * BC;
-        // ---- rotate Q and K pieces (cos/sin advanced by TSTRIDE per piece)
-        if (rotate) {
-            float cc[4], ss[4];
+        __builtin_amdgcn_s_waitcnt(0);  // this block's direct loads (and older memory ops) are done
+        __syncthreads();                // ... for every wave; the other buffer is free again
+        if (blk + 1 < nblocks) load_block(blk + 1, Kn, Vn);
+        if (kbi == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cc[i] = cs0[i].x;
-                ss[i] = cs0[i].y;
-            }
+            for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-            for (int it = 0; it < C::ITER; ++it) {
-                rq[it] = rot4(rq[it], cc, ss);
-                rk[it] = rot4(rk[it], cc, ss);
+                for (int ks = 0; ks < C::KS; ++ks) qreg[u][ks] = __builtin_bit_cast(bf16x8, qn[u][ks]);
+            if (ci > 0) flush();                      // previous chunk's outputs
+            if (ci + 1 < nchunks) prefetch_q(t0 + BC);
+            // ---- O^T = (S_old^T Q~^T) xi, then gamma^b S
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float nc = cc[i] * stc[i] - ss[i] * sts[i];
-                    const float ns = ss[i] * stc[i] + cc[i] * sts[i];
-                    cc[i] = nc;
-                    ss[i] = ns;
+            for (int u = 0; u < C::NQT; ++u) {
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 fa[C::CT], fb[C::CT];
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) fa[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 8 * g);
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    if (ks + 1 < C::KS) {
+#pragma unroll
+                        for (int ct = 0; ct < C::CT; ++ct)
+                            fb[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
+                    }
+                    sched_fence();
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(fa[ct], qreg[u][ks], oacc[u][ct]);
+                    sched_fence();
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct) fa[ct] = fb[ct];
                 }
-            }
-        }
+                const float x = xi[16 * qtile[u] + l16];
 #pragma unroll
-        for (int it = 0; it < C::ITER; ++it)
-            *reinterpret_cast<u32x4 *>(Xs + (tf + it * C::TSTRIDE) * C::XP + d0) = rq[it];
-        __syncthreads();  // Q~ staged; St holds S_old
-        bf16x8 qreg[C::NQT][C::KS];
-#pragma unroll
-        for (int u = 0; u < C::NQT; ++u)
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                qreg[u][ks] = ld_lds8(Xs + (16 * qtile[u] + l16) * C::XP + 32 * ks + 8 * g);
-        __syncthreads();  // every wave has its Q~ rows
-#pragma unroll
-        for (int it = 0; it < C::ITER; ++it)
-            *reinterpret_cast<u32x4 *>(Xs + (tf + it * C::TSTRIDE) * C::XP + d0) = rk[it];
-#pragma unroll
-        for (int it = 0; it < C::VITER; ++it) {
-            const int t = vt0 + it * VSTRIDE;
-            *reinterpret_cast<u32x4 *>(Vs + t * C::VP + vd0) = rv[it];
-            u32x4 z;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                z[i] = pack_bf16x2(__uint_as_float(rv[it][i] << 16) * zv[it],
-                                   __uint_as_float(rv[it][i] & 0xffff0000u) * zv[it]);
-            *reinterpret_cast<u32x4 *>(Vz + t * C::VP + vd0) = z;
-        }
-        if (ci + 1 < nchunks) prefetch_kv(t0 + BC);  // next chunk's loads fly during the compute
-        __syncthreads();  // K~, V, V zeta staged
-
-        // ---- state update S = gamma^b S + K~^T (V zeta s) on this wave's tiles
-#pragma unroll
-        for (int rt = 0; rt < C::RPW; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
-#pragma unroll 2
-        for (int s = 0; s < BC / 32; ++s) {
-            const int tb = 32 * s + 8 * g;  // first token of this lane group
-            bf16x8 bv[C::CPW];
-#pragma unroll
-            for (int ct = 0; ct < C::CPW; ++ct) {
-                const __bf16 *base = Vz + (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
-                bv[ct] = cat(lds_tr(base + (tb + (l16 >> 2)) * C::VP),
-                             lds_tr(base + (tb + 4 + (l16 >> 2)) * C::VP));
+                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
             }
 #pragma unroll
-            for (int rt = 0; rt < C::RPW; ++rt) {
-                const __bf16 *base = Xs + (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
-                const bf16x8 ak = cat(lds_tr(base + (tb + (l16 >> 2)) * C::XP),
-                                      lds_tr(base + (tb + 4 + (l16 >> 2)) * C::XP));
+            for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
-            }
+                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
         }
 
+        // ---- state update with this block: S += K~^T (V zeta s)
+        {
+            s16x4 vr[2][C::CPW][2], kr[2][C::RPW][2];  // raw fragments, double buffered
+            auto load_su = [&](int s, int slot) {
+                const int tb = 32 * s + 8 * g;
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) {
+                    const int col = (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
+                    vr[slot][ct][0] = lds_tr_b(Vc + C::voff(tb + (l16 >> 2), col));
+                    vr[slot][ct][1] = lds_tr_b(Vc + C::voff(tb + 4 + (l16 >> 2), col));
+                }
+#pragma unroll
+                for (int rt = 0; rt < C::RPW; ++rt) {
+                    const int col = (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
+                    kr[slot][rt][0] = lds_tr_b(Kc + C::koff(tb + (l16 >> 2), col));
+                    kr[slot][rt][1] = lds_tr_b(Kc + C::koff(tb + 4 + (l16 >> 2), col));
+                }
+            };
+            load_su(0, 0);
+#pragma unroll
+            for (int s = 0; s < C::KB / 32; ++s) {
+                if (s + 1 < C::KB / 32) load_su(s + 1, (s + 1) & 1);
+                sched_fence();
+                const int tb = 32 * s + 8 * g;  // first token (within the block) of this lane group
+                float z[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[e] = zet[kbi * C::KB + tb + e];
+                bf16x8 bv[C::CPW];
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bv[ct][e] = static_cast<__bf16>(bf(vr[s & 1][ct][0][e]) * z[e]);
+                        bv[ct][4 + e] = static_cast<__bf16>(bf(vr[s & 1][ct][1][e]) * z[4 + e]);
+                    }
+#pragma unroll
+                for (int rt = 0; rt < C::RPW; ++rt) {
+                    const bf16x8 ak = cat(kr[s & 1][rt][0], kr[s & 1][rt][1]);
+#pragma unroll
+                    for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
+                }
+                sched_fence();
+            }
+        }
+
+        // ---- intra-chunk part with this block's 4 key tiles, for each query
+        // tile that reaches them (a wave-uniform test): P^T tiles with decay,
+        // scale and causal mask in registers, packed as B operands, then
+        // O^T += V^T P^T
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u) {
             const int qt = qtile[u];
-            const int jq = 16 * qt + l16;  // this lane's query row within the chunk
-            // ---- O^T = (S_old^T Q~^T) xi   (four independent accumulators)
-            f32x4 oacc[C::CT];
+            if (kbi * C::KB > 16 * qt + 15) continue;
+            const int jq = 16 * qt + l16;
+            f32x4 acc[4];
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct)
-                    oacc[ct] = mfma16(ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g), qreg[u][ks],
-                                      oacc[ct]);
+            for (int v4 = 0; v4 < 4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
             {
-                const float x = xi[jq];
+                bf16x8 fa[4], fb[4];
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * x;
-            }
-            // ---- intra-chunk part, keys 0 .. 16qt+15, four key tiles at a time:
-            // P^T tiles (decay, scale and causal mask in registers) packed as
-            // B operands, then O^T += V^T P^T
-#pragma unroll 1
-            for (int kq = 0; kq < C::NKT; kq += 4) {
-                if (kq <= qt) {
-                    f32x4 acc[4];
+                for (int v4 = 0; v4 < 4; ++v4)
+                    fa[v4] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v4 + l16, 8 * g));
 #pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ++ks)
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    if (ks + 1 < C::KS) {
 #pragma unroll
                         for (int v4 = 0; v4 < 4; ++v4)
-                            if (kq + v4 <= qt)
-                                acc[v4] = mfma16(ld_lds8(Xs + (16 * (kq + v4) + l16) * C::XP + 32 * ks + 8 * g),
-                                                 qreg[u][ks], acc[v4]);
-                    bf16x8 pb[2];
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * (kq + v4) + 4 * g + r;
-                            const float x = (t <= jq) ? acc[v4][r] * dec[jq - t] : 0.f;
-                            pb[v4 / 2][4 * (v4 & 1) + r] = static_cast<__bf16>(x);
-                        }
-#pragma unroll
-                    for (int hs = 0; hs < 2; ++hs) {
-                        const int s = kq / 2 + hs;
-                        if (2 * s <= qt) {
-#pragma unroll
-                            for (int ct = 0; ct < C::CT; ++ct) {
-                                const __bf16 *base = Vs + ct * 16 + 4 * (l16 & 3);
-                                const s16x4 lo = lds_tr(base + (32 * s + 4 * g + (l16 >> 2)) * C::VP);
-                                const s16x4 hi = lds_tr(base + (32 * s + 16 + 4 * g + (l16 >> 2)) * C::VP);
-                                oacc[ct] = mfma16(cat(lo, hi), pb[hs], oacc[ct]);
-                            }
-                        }
+                            fb[v4] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v4 + l16, 32 * (ks + 1) + 8 * g));
                     }
+                    sched_fence();
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) acc[v4] = mfma16(fa[v4], qreg[u][ks], acc[v4]);
+                    sched_fence();
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) fa[v4] = fb[v4];
                 }
             }
-            if (u == C::NQT - 1 && ci + 1 < nchunks) prefetch_q(t0 + BC);
-            // ---- GroupNorm over the row (lanes l16, l16+16, +32, +48 share a query)
-            const size_t orow = ((size_t)b * c.T + t0 + jq) * c.H + h;
-            float sum = 0.f;
+            bf16x8 pb[2];
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) sum += oacc[ct][0] + oacc[ct][1] + oacc[ct][2] + oacc[ct][3];
-            sum += __shfl_xor(sum, 16, 64);
-            sum += __shfl_xor(sum, 32, 64);
-            const float mean = sum * (1.f / W);
-            float m2 = 0.f;
+            for (int v4 = 0; v4 < 4; ++v4)
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct)
+                for (int r = 0; r < 4; ++r) {
+                    const int t = kbi * C::KB + 16 * v4 + 4 * g + r;
+                    const float x = (t <= jq) ? acc[v4][r] * dec[jq - t] : 0.f;
+                    pb[v4 / 2][4 * (v4 & 1) + r] = static_cast<__bf16>(x);
+                }
+            {
+                s16x4 va[2][C::CT][2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m2 += (oacc[ct][r] - mean) * (oacc[ct][r] - mean);
-            m2 += __shfl_xor(m2, 16, 64);
-            m2 += __shfl_xor(m2, 32, 64);
-            const bool gn = !(c.flags & MSR_FLAG_NO_GROUPNORM);
-            float mu = 0.f, inv = 1.f;
-            if (gn && a.NS == 1) {
-                mu = mean;
-                inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
-            } else if (gn && g == 0) {
-                a.stats[orow * a.NS + slice] = make_float2(mean, m2);
-            }
-            uint16_t *dst = a.o + orow * c.dv + col0 + 4 * g;
+                for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 v4;
+                    for (int ct = 0; ct < C::CT; ++ct) {
+                        const int col = ct * 16 + 4 * (l16 & 3);
+                        va[hs][ct][0] = lds_tr_b(Vc + C::voff(32 * hs + 4 * g + (l16 >> 2), col));
+                        va[hs][ct][1] = lds_tr_b(Vc + C::voff(32 * hs + 16 + 4 * g + (l16 >> 2), col));
+                    }
+                sched_fence();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v4[r] = static_cast<__bf16>((oacc[ct][r] - mu) * inv);
-                *reinterpret_cast<bf16x4 *>(dst + ct * 16) = v4;
+                for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        oacc[u][ct] = mfma16(cat(va[hs][ct][0], va[hs][ct][1]), pb[hs], oacc[u][ct]);
             }
         }
-        __syncthreads();  // every wave is done with Xs, Vs, Vz and St
-        write_st();
+
+        if (kbi == C::NB - 1) {
+            // ---- GroupNorm over each row (lanes l16, l16+16, +32, +48 share a query)
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u) {
+                const int jq = 16 * qtile[u] + l16;
+                float sum = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct)
+                    sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                const float mean = sum * (1.f / W);
+                float m2 = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m2 += (oacc[u][ct][r] - mean) * (oacc[u][ct][r] - mean);
+                m2 += __shfl_xor(m2, 16, 64);
+                m2 += __shfl_xor(m2, 32, 64);
+                float mu = 0.f, inv = 1.f;
+                if (a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+                    mu = mean;
+                    inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
+                }
+                // stored one chunk later (flush), so that waiting for the next
+                // blocks' loads does not also wait for these stores
+                pend_row[u] = ((size_t)b * c.T + t0 + jq) * c.H + h;
+                pend_stat[u] = make_float2(mean, m2);
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) {
+                    pend_o[u][ct][0] = pack_bf16x2((oacc[u][ct][0] - mu) * inv, (oacc[u][ct][1] - mu) * inv);
+                    pend_o[u][ct][1] = pack_bf16x2((oacc[u][ct][2] - mu) * inv, (oacc[u][ct][3] - mu) * inv);
+                }
+            }
+            if (C::NB == 1) __syncthreads();  // every wave has read S_old^T
+            write_st();
+        }
+    };
+    for (int blk = 0; blk < nblocks; blk += 2) {
+        step(blk, Kb0, Vb0, Kb1, Vb1);
+        if (blk + 1 < nblocks) step(blk + 1, Kb1, Vb1, Kb0, Vb0);
     }
+    if (nchunks > 0) flush();
 
     if (a.s_out) {
 #pragma unroll
@@ -453,6 +508,38 @@ __global__ void angle_table_kernel(MsrConst c, float2 *cs) {
         float co, si;
         rot_cos_sin(c.pos0 + t, c.theta[i], co, si);
         cs[e] = make_float2(co, si);
+    }
+}
+
+// theta_shift of Q and K into bf16 copies, once per token and head: pair i
+// of the token at position pos0 + t becomes (x0 c - x1 s, x1 c + x0 s) with
+// (c, s) from the angle table; fp32 arithmetic.  8 channels per thread.
+__global__ void rotate_qk_kernel(MsrConst c, const float2 *__restrict__ cs,
+                                 const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                 uint16_t *__restrict__ qr, uint16_t *__restrict__ kr) {
+    const int p8 = c.dk / 8;
+    const size_t n = (size_t)c.B * c.T * c.H * p8;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const int d8 = (int)(e % p8);
+        const size_t row = e / p8;  // (b * T + t) * H + h
+        const int t = (int)((row / c.H) % c.T);
+        const float4 *cp = reinterpret_cast<const float4 *>(cs + (size_t)t * (c.dk / 2) + 4 * d8);
+        const float4 c01 = cp[0], c23 = cp[1];
+        const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+        const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
+        const u32x4 uq = reinterpret_cast<const u32x4 *>(q)[e];
+        const u32x4 uk = reinterpret_cast<const u32x4 *>(k)[e];
+        u32x4 oq, ok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x0 = __uint_as_float(uq[i] << 16), x1 = __uint_as_float(uq[i] & 0xffff0000u);
+            oq[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
+            x0 = __uint_as_float(uk[i] << 16);
+            x1 = __uint_as_float(uk[i] & 0xffff0000u);
+            ok[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
+        }
+        reinterpret_cast<u32x4 *>(qr)[e] = oq;
+        reinterpret_cast<u32x4 *>(kr)[e] = ok;
     }
 }
 
@@ -496,11 +583,8 @@ template <int DK, int BC>
 hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, hipStream_t st) {
     using C = Cfg<DK, BC>;
     auto kern = chunk_mfma_kernel<DK, BC>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    if (e != hipSuccess) return e;
     const int grid = c.B * c.H * a.NS;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, st, c, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), 0, st, c, a);
     return hipGetLastError();
 }
 
@@ -509,22 +593,24 @@ hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, hipStre
     switch (chunk) {
     case 64: return launch_chunk<DK, 64>(c, a, st);
     case 128: return launch_chunk<DK, 128>(c, a, st);
-    case 256:
-        if constexpr (DK <= 128) return launch_chunk<DK, 256>(c, a, st);
-        return hipErrorNotSupported;
+    case 256: return launch_chunk<DK, 256>(c, a, st);
     default: return hipErrorNotSupported;
     }
 }
 
 struct MfmaPlan {
-    size_t cs = 0, stats = 0, total = 0;
+    size_t cs = 0, qr = 0, kr = 0, stats = 0, total = 0;
 };
 
+// workspace: [cos/sin table][Q~ bf16][K~ bf16][slice statistics]
 MfmaPlan mfma_plan(const msr_problem *p) {
     MfmaPlan m;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t qk = (size_t)p->B * p->T * p->H * p->dk * 2;
     m.cs = 0;
-    m.stats = up((size_t)p->T * (p->dk / 2) * sizeof(float2));
+    m.qr = up((size_t)p->T * (p->dk / 2) * sizeof(float2));
+    m.kr = m.qr + up(qk);
+    m.stats = m.kr + up(qk);
     const int NS = p->dv / W;
     m.total = m.stats + (NS > 1 ? up((size_t)p->B * p->T * p->H * NS * sizeof(float2)) : 0);
     return m;
@@ -537,8 +623,9 @@ bool mfma_supported(const msr_problem *p, int form, int chunk) {
     if (p->dk != 64 && p->dk != 128 && p->dk != 256) return false;
     if (p->dv % W != 0) return false;
     if (chunk != 64 && chunk != 128 && chunk != 256) return false;
-    if (p->dk == 256 && chunk == 256) return false;
     if (chunk > p->T || p->T % chunk != 0) return false;
+    // per-thread byte offsets within one batch row are 32-bit
+    if ((uint64_t)p->T * p->H * (p->dk > p->dv ? p->dk : p->dv) * 2 >= (1ull << 32)) return false;
     return true;
 }
 
@@ -552,24 +639,33 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
                           void *ws, hipStream_t st) {
     const MfmaPlan m = mfma_plan(p);
     char *wsb = static_cast<char *>(ws);
+    const bool rotate = !(c.flags & MSR_FLAG_NO_ROTATE);
     ChunkArgs a;
-    a.q = static_cast<const uint16_t *>(Q);
-    a.k = static_cast<const uint16_t *>(K);
+    a.q = rotate ? reinterpret_cast<const uint16_t *>(wsb + m.qr) : static_cast<const uint16_t *>(Q);
+    a.k = rotate ? reinterpret_cast<const uint16_t *>(wsb + m.kr) : static_cast<const uint16_t *>(K);
     a.v = static_cast<const uint16_t *>(V);
     a.o = static_cast<uint16_t *>(O);
     a.s_in = s_in;
     a.s_out = s_out;
-    a.cs = reinterpret_cast<float2 *>(wsb + m.cs);
     a.NS = p->dv / W;
     a.stats = a.NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
 
-    const size_t ncs = (size_t)p->T * (p->dk / 2);
-    size_t g = (ncs + 255) / 256;
-    if (g > 65536) g = 65536;
-    hipLaunchKernelGGL(angle_table_kernel, dim3((unsigned)g), dim3(256), 0, st, c,
-                       reinterpret_cast<float2 *>(wsb + m.cs));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (rotate) {
+        float2 *cs = reinterpret_cast<float2 *>(wsb + m.cs);
+        const size_t ncs = (size_t)p->T * (p->dk / 2);
+        size_t g = (ncs + 255) / 256;
+        if (g > 65536) g = 65536;
+        hipLaunchKernelGGL(angle_table_kernel, dim3((unsigned)g), dim3(256), 0, st, c, cs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const size_t n8 = (size_t)p->B * p->T * p->H * (p->dk / 8);
+        g = (n8 + 255) / 256;
+        if (g > 262144) g = 262144;
+        hipLaunchKernelGGL(rotate_qk_kernel, dim3((unsigned)g), dim3(256), 0, st, c, cs,
+                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
+                           reinterpret_cast<uint16_t *>(wsb + m.qr), reinterpret_cast<uint16_t *>(wsb + m.kr));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     switch (p->dk) {
     case 64: e = dispatch_bc<64>(c, a, chunk, st); break;
     case 128: e = dispatch_bc<128>(c, a, chunk, st); break;

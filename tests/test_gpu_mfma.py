@@ -19,6 +19,7 @@ CASES = [  # (B, T, H, dk, dv, chunk)
     (2, 384, 2, 128, 256, 128),
     (1, 512, 1, 128, 128, 256),
     (1, 192, 2, 256, 64, 64),
+    (1, 512, 1, 256, 128, 256),
     (1, 384, 2, 256, 192, 128),
 ]
 
