@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-scale retention hot path on one MI355X.
+
+One "step" is one chunkwise forward (rotation prologue, intra-chunk MFMA
+products, decay mask, cross-chunk term, state carry, GroupNorm) over the
+7B-shaped layer: B=2, T=8192, H=16, d_k=256, d_v=512, chunk 128, bf16 in,
+fp32 state.  `value` is that forward's throughput in tokens/s with inputs
+already resident in HBM.  The same JSON line also reports
+  - roofline: the chunk-recurrence kernel alone, timed with HIP events
+    recorded around it on its own stream (library measurement hook), against
+    the bf16 dense MFMA peak, with algorithmic flops
+    F = (b+1)(d_k+d_v) + 4 d_k d_v per token and head;
+  - decode: the recurrent decode step at B=64, H=16, d_k=256, d_v=512 after a
+    2048-token chunkwise prefill, 1024 steps, against the HBM peak;
+  - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
+    of the same workload on the host cores (a reported baseline only).
+Inputs are synthetic and seeded.  Usage:
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+MFMA_BF16_PEAK_TFLOPS = 2516.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
+
+
+class HipEvents:
+    """hipEvent pairs created through the HIP runtime (the library records
+    them around its main kernel on the launch stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float(0.0)
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.pairs[i][0]),
+                                          ctypes.c_void_p(self.pairs[i][1]))
+        if rc:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(a))
+            self.hip.hipEventDestroy(ctypes.c_void_p(b))
+
+
+def chunk_flops(T, H, B, dk, dv, b):
+    return B * T * H * ((b + 1) * (dk + dv) + 4 * dk * dv)
+
+
+def chunk_bytes(T, H, B, dk, dv):
+    return B * T * H * (2 * dk + 2 * dv) * 2
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "retnet_scale_retention_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE measurement, if it was taken on the current kernel sources."""
+    p = ROOT / "profiles" / "traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text()).get(kernel)
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
+    w = mi.WORKLOADS["7b"]
+    dev = torch.device("cuda:0")
+    q, k, v = mi.qkv(w)
+    up = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    g = mi.gammas(w.H)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g,
+                                        msr.MSR_FORM_CHUNKWISE, chunk), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+    ev = HipEvents(steps)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        msr.set_kernel_events(*ev.pairs[i])
+        msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+    msr.set_kernel_events(None, None)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = [ev.elapsed_ms(i) for i in range(steps)]
+    ev.close()
+    ms = total_ms / steps
+    kms = float(np.mean(kern_ms))
+    flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
+    return {
+        "workload": w, "chunk": chunk, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+        "kernel_ms": kms, "flops": flops, "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
+        "kernel_tflops": flops / (kms / 1e3) / 1e12,
+    }
+
+
+def bench_decode(torch, msr, mi, nsteps):
+    w = mi.WORKLOADS["decode"]
+    dev = torch.device("cuda:0")
+    g = mi.gammas(w.H)
+    # prefill (chunkwise, chunk 128) seeds the state
+    q = mi.device_normal((w.B, w.T, w.H, w.dk), 3001, dev, torch.bfloat16)
+    k = mi.device_normal((w.B, w.T, w.H, w.dk), 3002, dev, torch.bfloat16)
+    v = mi.device_normal((w.B, w.T, w.H, w.dv), 3003, dev, torch.bfloat16)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    _, state = msr.msr_chunkwise(q, k, v, g, 128)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - tp0) * 1e3
+    del q, k, v
+    qs = mi.device_normal((nsteps, w.B, w.H, w.dk), 3004, dev, torch.bfloat16)
+    ks = mi.device_normal((nsteps, w.B, w.H, w.dk), 3005, dev, torch.bfloat16)
+    vs = mi.device_normal((nsteps, w.B, w.H, w.dv), 3006, dev, torch.bfloat16)
+    o = torch.empty((w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    for i in range(3):  # warm-up on a copy of the state
+        st = state.clone()
+        msr.msr_recurrent_step(qs[i], ks[i], vs[i], st, g, w.T + i, out=o)
+    ev = HipEvents(nsteps)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(nsteps):
+        msr.set_kernel_events(*ev.pairs[i])
+        msr.msr_recurrent_step(qs[i], ks[i], vs[i], state, g, w.T + i, out=o)
+    msr.set_kernel_events(None, None)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kern = [ev.elapsed_ms(i) for i in range(nsteps)]
+    ev.close()
+    step_ms = total_ms / nsteps
+    kms = float(np.mean(kern))
+    bytes_step = 2 * w.B * w.H * w.dk * w.dv * 4 + w.B * w.H * (2 * w.dk + 2 * w.dv) * 2
+    return {
+        "config": {"B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "prefill_tokens": w.T, "steps": nsteps},
+        "steps_per_s": 1e3 / step_ms, "tokens_per_s": w.B * 1e3 / step_ms,
+        "ms_per_step": step_ms, "kernel_us": kms * 1e3,
+        "hbm": {"achieved": bytes_step / (kms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": bytes_step / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": bytes_step},
+        "prefill_ms": prefill_ms,
+    }
+
+
+def cpu_baseline(mi, chunk):
+    """The oracle's chunkwise form on a bounded sample of the 7B workload:
+    16 (batch, head) pairs x 4096 tokens, scaled linearly to the full B*T*H
+    token-heads (the form's cost is linear in tokens and pairs)."""
+    from oracle import oracle
+    w = mi.WORKLOADS["7b"]
+    Ts, Hs = 4096, 16
+    q, k, v = mi.qkv(w, T=Ts)
+    q, k, v = (x[:1, :, :Hs] for x in (q, k, v))
+    g = mi.gammas(w.H)[:Hs]
+    t0 = time.perf_counter()
+    oracle.chunkwise(q, k, v, g, chunk)
+    dt = time.perf_counter() - t0
+    token_heads = Ts * Hs
+    full = w.B * w.T * w.H
+    tokens_per_s = w.B * w.T / (dt * full / token_heads)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"chunkwise form, chunk {chunk}, 16 heads x 4096 tokens of the 7B-shaped layer "
+                      f"({dt:.1f} s), scaled to B*T*H = {full} token-heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the operator runs on a single MI355X here "
+              "(the (batch, head) pairs would shard across GPUs with no communication); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import msr_inputs as mi
+    import retnet_scale_retention_amd as msr
+    msr.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    r = bench_chunkwise(torch, msr, mi, args.steps, args.warmup, args.chunk)
+    w = r["workload"]
+    dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
+    cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
+    traffic = traffic_record("chunk_mfma_kernel")
+    line = {
+        "metric": "chunkwise MSR fwd tokens/s + decode steps/s; % of bf16 MFMA / HBM peak",
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "7B-shaped MSR layer chunkwise forward", "B": w.B, "T": w.T, "H": w.H,
+                   "dk": w.dk, "dv": w.dv, "chunk": r["chunk"], "state": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": r["kernel_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": r["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic, "kernel": "chunk_mfma_kernel",
+                     "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["flops"]},
+        "cpu_baseline": cpu,
+        "decode": dec,
+        "hbm_view": {"bytes_per_step": r["bytes"],
+                     "achieved_GBs": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9,
+                     "frac": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,8 +51,9 @@
  *   - Scratch memory only ever comes from the caller's workspace `ws`, sized
  *     by msr_workspace_size().  Calls that share a workspace must be ordered
  *     on one stream.
- *   - The library is stateless apart from the per-thread error text, so calls
- *     from several host threads are safe when their buffers are distinct.
+ *   - The library keeps no state apart from per-thread error text and the
+ *     per-thread measurement hook, so calls from several host threads are
+ *     safe when their buffers are distinct.
  */
 #ifndef MSR_H
 #define MSR_H
@@ -146,6 +147,17 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
  */
 msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k,
                               const void *v, void *o, float *state, void *hip_stream);
+
+/*
+ * Measurement hook (optional).  When `start` and `stop` are non-NULL
+ * hipEvent_t handles, each later compute call made on this host thread
+ * records `start` on its stream immediately before its main kernel and
+ * `stop` immediately after it: the chunk-recurrence kernel of msr_chunkwise,
+ * the output kernel of msr_parallel, the kernel of msr_recurrent_step.  The
+ * caller owns the events; NULL, NULL switches the hook off.  The hook only
+ * records events: results are unchanged.
+ */
+void msr_set_kernel_events(void *start, void *stop);
 
 #ifdef __cplusplus
 }

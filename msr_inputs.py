@@ -109,3 +109,12 @@ def decode_token(w: Workload, s: int):
 def state(w: Workload, scale: float = 1.0):
     """A seeded fp32 incoming state [B, H, dk, dv]."""
     return (normal((w.seed, S_IN), (w.B, w.H, w.dk, w.dv)) * np.float32(scale)).astype(np.float32)
+
+
+def device_normal(shape, seed: int, device, dtype):
+    """N(0, 1) tensor drawn on the device by torch's Philox generator seeded
+    with `seed` (for inputs too large to draw on the host), cast to dtype."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)

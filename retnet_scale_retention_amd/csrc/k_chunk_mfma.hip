@@ -80,11 +80,13 @@ __device__ __forceinline__ bf16x8 ld_lds8(const __bf16 *p) {
 
 template <int DK, int BC>
 struct Cfg {
-    static constexpr int KB = 64;                        // keys per LDS block
+    static constexpr int KB = 32;                        // keys per LDS block (one k-step)
     static constexpr int NB = BC / KB;                   // key blocks per chunk
     static constexpr int NKT = BC / 16;                  // 16-token tiles per chunk
-    static constexpr int NW = NKT >= 4 ? NKT / 2 : NKT;  // waves (two query tiles each)
-    static constexpr int NQT = NKT / NW;                 // query tiles per wave (1 or 2)
+    // waves and query tiles per wave: two tiles per wave (fragment reuse)
+    // except for the smallest chunk
+    static constexpr int NQT = NKT >= 8 ? 2 : 1;
+    static constexpr int NW = NKT / NQT;
     static constexpr int THREADS = NW * 64;
     static constexpr int CT = W / 16;          // state / output column tiles
     static constexpr int NT = (DK / 16) * CT;  // state tiles per workgroup
@@ -93,24 +95,22 @@ struct Cfg {
     static constexpr int RPW = TPW / CPW;            // ... and row tiles
     static constexpr int CG = CT / CPW;              // column groups of waves
     static constexpr int KS = DK / 32;      // k-steps over d_k
-    static constexpr int KROW = DK * 2;     // bytes per K~ row in LDS (unpadded, swizzled)
+    static constexpr int KROW = DK * 2;     // bytes per K~ / Q~ row in LDS (swizzled)
     static constexpr int KBLK = KB * KROW;  // bytes per K~ block
     static constexpr int VROW = W * 2;      // bytes per V row
     static constexpr int VBLK = KB * VROW;  // bytes per V block
-    static constexpr int KUPW = KBLK / 1024 / NW;  // 1 KiB direct loads per wave per K~ block
-    static constexpr int VUPW = VBLK / 1024 / NW;  // ... per V block
+    static constexpr bool QLDS = BC * DK <= 32768;   // next chunk's Q~ staged in LDS
+    static constexpr int QBLK = QLDS ? BC * KROW : 16;
     static constexpr int SP = DK + 8;       // padded LDS row of S^T (bf16)
-    static constexpr size_t LDS_BYTES = 2 * (size_t)KBLK + 2 * (size_t)VBLK + (size_t)W * SP * 2 + 3 * BC * 4;
-    static_assert(NKT % NW == 0 && NQT <= 2, "query tiles split over waves");
+    static_assert(NKT % NQT == 0 && NW <= 16, "query tiles split over waves");
     static_assert(NT % NW == 0 && TPW >= 1, "state tiles must split evenly over waves");
-    static_assert(KUPW >= 1 && KUPW * NW * 1024 == KBLK, "K~ block loads");
-    static_assert(VUPW >= 1 && VUPW * NW * 1024 == VBLK, "V block loads");
-    static_assert(LDS_BYTES <= 163840, "LDS budget");
+    static_assert(KBLK % 1024 == 0 && VBLK % 1024 == 0, "1 KiB direct-load units");
+    static_assert(2 * KBLK + 2 * VBLK + QBLK + W * SP * 2 + 3 * BC * 4 <= 163840, "LDS budget");
     // XOR swizzle of the 16-byte chunks of a row: 16 consecutive rows read
     // at one logical chunk hit 16 different bank groups
     __device__ static int swz_k(int row) { return DK >= 128 ? (row & 15) : ((row >> 1) & 7); }
     __device__ static int swz_v(int row) { return (row >> 1) & 7; }
-    __device__ static int koff(int row, int col) {  // byte offset of K~[row][col] in a block
+    __device__ static int koff(int row, int col) {  // byte offset of K~[row][col] (also Q~)
         return row * KROW + ((((col >> 3) ^ swz_k(row))) << 4) + (col & 7) * 2;
     }
     __device__ static int voff(int row, int col) {
@@ -150,6 +150,13 @@ __device__ __forceinline__ void load_lds16(const void *gptr, void *lds) {
 // current one.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ s16x4 lds_tr_b(const char *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
 }
@@ -157,10 +164,11 @@ __device__ __forceinline__ s16x4 lds_tr_b(const char *p) {
 template <int DK, int BC>
 __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
-    // two separate K~/V buffers (distinct LDS objects, so the compiler can
-    // tell that the direct loads into one do not alias reads of the other)
+    // separate LDS objects for the two block buffers and the Q~ tile, so the
+    // compiler can tell the direct loads into one from reads of another
     __shared__ __attribute__((aligned(16))) char Kb0[C::KBLK], Kb1[C::KBLK];
     __shared__ __attribute__((aligned(16))) char Vb0[C::VBLK], Vb1[C::VBLK];
+    __shared__ __attribute__((aligned(16))) char Qs[C::QBLK];
     __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_old^T
     __shared__ float dec[BC], xi[BC], zet[BC];  // s gamma^d, gamma^(j+1), s gamma^(BC-1-t)
 
@@ -199,36 +207,40 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const char *kb = reinterpret_cast<const char *>(a.k + ((size_t)b * c.T * c.H + h) * DK);
     const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
 
-    // direct loads of key block `blk` (global index over the sequence) into buffer `buf`
-    auto load_block = [&](int blk, char *Kd, char *Vd) {
-        const int tok0 = blk * C::KB;
-#pragma unroll
-        for (int i = 0; i < C::KUPW; ++i) {
-            const int byte = (w * C::KUPW + i) * 1024 + lane * 16;  // position in the block
+    // direct loads of 1 KiB units: unit u of a [rows][row bytes] tile whose
+    // row r starts at global byte base + r * rstride; units go round-robin
+    // over the waves
+    auto dma_k = [&](const char *gbase, int tok0, char *dst, int nbytes) {
+        for (int u = w; u < nbytes / 1024; u += C::NW) {
+            const int byte = u * 1024 + lane * 16;
             const int row = byte / C::KROW, phys = (byte % C::KROW) >> 4;
-            const int chunk = phys ^ C::swz_k(row);
-            load_lds16(kb + (uint32_t)(tok0 + row) * rowQK + chunk * 16, Kd + (w * C::KUPW + i) * 1024);
+            load_lds16(gbase + (uint32_t)(tok0 + row) * rowQK + (phys ^ C::swz_k(row)) * 16, dst + u * 1024);
         }
-#pragma unroll
-        for (int i = 0; i < C::VUPW; ++i) {
-            const int byte = (w * C::VUPW + i) * 1024 + lane * 16;
+    };
+    auto dma_v = [&](int tok0, char *dst) {
+        for (int u = w; u < C::VBLK / 1024; u += C::NW) {
+            const int byte = u * 1024 + lane * 16;
             const int row = byte / C::VROW, phys = (byte % C::VROW) >> 4;
-            const int chunk = phys ^ C::swz_v(row);
-            load_lds16(vb + (uint32_t)(tok0 + row) * rowV + chunk * 16, Vd + (w * C::VUPW + i) * 1024);
+            load_lds16(vb + (uint32_t)(tok0 + row) * rowV + (phys ^ C::swz_v(row)) * 16, dst + u * 1024);
         }
     };
 
-    // query tiles of this wave: w and, when there are two, NKT-1-w
+    // query tiles of this wave: w and, with two, NKT-1-w (balances the causal work)
     int qtile[C::NQT];
     qtile[0] = w;
     if (C::NQT == 2) qtile[C::NQT - 1] = C::NKT - 1 - w;
-    u32x4 qn[C::NQT][C::KS];  // next chunk's Q~ rows, MFMA operand layout
-    auto prefetch_q = [&](int t0) {
+    bf16x8 qreg[C::NQT][C::KS];  // this chunk's Q~ rows in MFMA operand layout
+    auto take_q = [&](int t0) {
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                qn[u][ks] = ld16(qb, (uint32_t)(t0 + 16 * qtile[u] + l16) * rowQK + (32 * ks + 8 * g) * 2);
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const int row = 16 * qtile[u] + l16, col = 32 * ks + 8 * g;
+                if constexpr (C::QLDS)
+                    qreg[u][ks] = *reinterpret_cast<const bf16x8 *>(Qs + C::koff(row, col));
+                else
+                    qreg[u][ks] = __builtin_bit_cast(bf16x8, ld16(qb, (uint32_t)(t0 + row) * rowQK + col * 2));
+            }
     };
 
     // ---- state tiles of this wave: rows (rg*RPW + rt)*16 + 4g + r, cols (cg*CPW + ct)*16 + l16
@@ -281,50 +293,60 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 
     const int nchunks = c.T / BC;
     const int nblocks = nchunks * C::NB;
-    if (nblocks > 0) {
-        load_block(0, Kb0, Vb0);
-        prefetch_q(0);
-    }
     write_st();
+    if (nblocks > 0) {
+        if constexpr (C::QLDS) dma_k(qb, 0, Qs, C::QBLK);
+        dma_k(kb, 0, Kb0, C::KBLK);
+        dma_v(0, Vb0);
+    }
 
-    bf16x8 qreg[C::NQT][C::KS];
     f32x4 oacc[C::NQT][C::CT];
     // one key block: compute on (Kc, Vc) while the next block streams into (Kn, Vn)
     auto step = [&](int blk, const char *Kc, const char *Vc, char *Kn, char *Vn) {
         const int ci = blk / C::NB, kbi = blk % C::NB;
         const int t0 = ci * BC;
-        __builtin_amdgcn_s_waitcnt(0);  // this block's direct loads (and older memory ops) are done
-        __syncthreads();                // ... for every wave; the other buffer is free again
-        if (blk + 1 < nblocks) load_block(blk + 1, Kn, Vn);
+        // this block's direct loads (issued one step ago) are complete; the
+        // Q~ tile of the next chunk, issued last in the previous step, may
+        // still be in flight
+        if (kbi == 1 && C::QLDS && ci + 1 < nchunks)
+            wait_vm<0>();  // (nothing newer to spare at this point)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
         if (kbi == 0) {
+            take_q(t0);
+            if (ci > 0) flush();  // previous chunk's outputs
+        }
+        if (blk + 1 < nblocks) {
+            dma_k(kb, (blk + 1) * C::KB, Kn, C::KBLK);
+            dma_v((blk + 1) * C::KB, Vn);
+        }
+        if (kbi == 0) {
+            // ---- O^T = (S_old^T Q~^T) xi for every query tile, then gamma^b S
+            bf16x8 fa[C::CT], fb[C::CT];
 #pragma unroll
             for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) qreg[u][ks] = __builtin_bit_cast(bf16x8, qn[u][ks]);
-            if (ci > 0) flush();                      // previous chunk's outputs
-            if (ci + 1 < nchunks) prefetch_q(t0 + BC);
-            // ---- O^T = (S_old^T Q~^T) xi, then gamma^b S
-#pragma unroll
-            for (int u = 0; u < C::NQT; ++u) {
-#pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                bf16x8 fa[C::CT], fb[C::CT];
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) fa[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 8 * g);
+            for (int ct = 0; ct < C::CT; ++ct) fa[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 8 * g);
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) {
-                    if (ks + 1 < C::KS) {
+            for (int ks = 0; ks < C::KS; ++ks) {
+                if (ks + 1 < C::KS) {
 #pragma unroll
-                        for (int ct = 0; ct < C::CT; ++ct)
-                            fb[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
-                    }
-                    sched_fence();
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        fb[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
+                }
+                sched_fence();
+#pragma unroll
+                for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
                     for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(fa[ct], qreg[u][ks], oacc[u][ct]);
-                    sched_fence();
+                sched_fence();
 #pragma unroll
-                    for (int ct = 0; ct < C::CT; ++ct) fa[ct] = fb[ct];
-                }
+                for (int ct = 0; ct < C::CT; ++ct) fa[ct] = fb[ct];
+            }
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u) {
                 const float x = xi[16 * qtile[u] + l16];
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
@@ -334,109 +356,104 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 #pragma unroll
                 for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
         }
+        // the next chunk's Q~ tile may be overwritten once every wave has
+        // taken this chunk's rows (they all passed this step's barrier)
+        if (C::QLDS && kbi == 1 && ci + 1 < nchunks) dma_k(qb, t0 + BC, Qs, C::QBLK);
 
-        // ---- state update with this block: S += K~^T (V zeta s)
+        // ---- state update with this block's 32 tokens: S += K~^T (V zeta s)
         {
-            s16x4 vr[2][C::CPW][2], kr[2][C::RPW][2];  // raw fragments, double buffered
-            auto load_su = [&](int s, int slot) {
-                const int tb = 32 * s + 8 * g;
+            const int tb = 8 * g;  // first token (within the block) of this lane group
+            s16x4 vr[C::CPW][2], kr[C::RPW][2];
 #pragma unroll
-                for (int ct = 0; ct < C::CPW; ++ct) {
-                    const int col = (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
-                    vr[slot][ct][0] = lds_tr_b(Vc + C::voff(tb + (l16 >> 2), col));
-                    vr[slot][ct][1] = lds_tr_b(Vc + C::voff(tb + 4 + (l16 >> 2), col));
+            for (int ct = 0; ct < C::CPW; ++ct) {
+                const int col = (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
+                vr[ct][0] = lds_tr_b(Vc + C::voff(tb + (l16 >> 2), col));
+                vr[ct][1] = lds_tr_b(Vc + C::voff(tb + 4 + (l16 >> 2), col));
+            }
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt) {
+                const int col = (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
+                kr[rt][0] = lds_tr_b(Kc + C::koff(tb + (l16 >> 2), col));
+                kr[rt][1] = lds_tr_b(Kc + C::koff(tb + 4 + (l16 >> 2), col));
+            }
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = zet[kbi * C::KB + tb + e];
+            bf16x8 bv[C::CPW];
+#pragma unroll
+            for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bv[ct][e] = static_cast<__bf16>(bf(vr[ct][0][e]) * z[e]);
+                    bv[ct][4 + e] = static_cast<__bf16>(bf(vr[ct][1][e]) * z[4 + e]);
                 }
 #pragma unroll
-                for (int rt = 0; rt < C::RPW; ++rt) {
-                    const int col = (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
-                    kr[slot][rt][0] = lds_tr_b(Kc + C::koff(tb + (l16 >> 2), col));
-                    kr[slot][rt][1] = lds_tr_b(Kc + C::koff(tb + 4 + (l16 >> 2), col));
-                }
-            };
-            load_su(0, 0);
+            for (int rt = 0; rt < C::RPW; ++rt) {
+                const bf16x8 ak = cat(kr[rt][0], kr[rt][1]);
 #pragma unroll
-            for (int s = 0; s < C::KB / 32; ++s) {
-                if (s + 1 < C::KB / 32) load_su(s + 1, (s + 1) & 1);
-                sched_fence();
-                const int tb = 32 * s + 8 * g;  // first token (within the block) of this lane group
-                float z[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) z[e] = zet[kbi * C::KB + tb + e];
-                bf16x8 bv[C::CPW];
-#pragma unroll
-                for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bv[ct][e] = static_cast<__bf16>(bf(vr[s & 1][ct][0][e]) * z[e]);
-                        bv[ct][4 + e] = static_cast<__bf16>(bf(vr[s & 1][ct][1][e]) * z[4 + e]);
-                    }
-#pragma unroll
-                for (int rt = 0; rt < C::RPW; ++rt) {
-                    const bf16x8 ak = cat(kr[s & 1][rt][0], kr[s & 1][rt][1]);
-#pragma unroll
-                    for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
-                }
-                sched_fence();
+                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
             }
         }
 
-        // ---- intra-chunk part with this block's 4 key tiles, for each query
-        // tile that reaches them (a wave-uniform test): P^T tiles with decay,
-        // scale and causal mask in registers, packed as B operands, then
-        // O^T += V^T P^T
+        // ---- intra-chunk part with this block's two 16-key tiles for the
+        // query tiles that reach them (wave-uniform tests): P^T tiles with
+        // decay, scale and causal mask in registers, packed as B operands,
+        // then O^T += V^T P^T
+        bool need[C::NQT];
+        bool any = false;
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u) {
-            const int qt = qtile[u];
-            if (kbi * C::KB > 16 * qt + 15) continue;
-            const int jq = 16 * qt + l16;
-            f32x4 acc[4];
+            need[u] = kbi * C::KB <= 16 * qtile[u] + 15;
+            any = any || need[u];
+        }
+        if (any) {
+            f32x4 acc[C::NQT][2];
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            {
-                bf16x8 fa[4], fb[4];
+            for (int u = 0; u < C::NQT; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 fa[2], fb[2];
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    fa[v4] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v4 + l16, 8 * g));
+            for (int v2 = 0; v2 < 2; ++v2)
+                fa[v2] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v2 + l16, 8 * g));
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) {
-                    if (ks + 1 < C::KS) {
+            for (int ks = 0; ks < C::KS; ++ks) {
+                if (ks + 1 < C::KS) {
 #pragma unroll
-                        for (int v4 = 0; v4 < 4; ++v4)
-                            fb[v4] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v4 + l16, 32 * (ks + 1) + 8 * g));
-                    }
-                    sched_fence();
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) acc[v4] = mfma16(fa[v4], qreg[u][ks], acc[v4]);
-                    sched_fence();
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) fa[v4] = fb[v4];
+                    for (int v2 = 0; v2 < 2; ++v2)
+                        fb[v2] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v2 + l16, 32 * (ks + 1) + 8 * g));
                 }
-            }
-            bf16x8 pb[2];
+                sched_fence();
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4)
+                for (int u = 0; u < C::NQT; ++u)
+                    if (need[u]) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = kbi * C::KB + 16 * v4 + 4 * g + r;
-                    const float x = (t <= jq) ? acc[v4][r] * dec[jq - t] : 0.f;
-                    pb[v4 / 2][4 * (v4 & 1) + r] = static_cast<__bf16>(x);
-                }
-            {
-                s16x4 va[2][C::CT][2];
-#pragma unroll
-                for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-                    for (int ct = 0; ct < C::CT; ++ct) {
-                        const int col = ct * 16 + 4 * (l16 & 3);
-                        va[hs][ct][0] = lds_tr_b(Vc + C::voff(32 * hs + 4 * g + (l16 >> 2), col));
-                        va[hs][ct][1] = lds_tr_b(Vc + C::voff(32 * hs + 16 + 4 * g + (l16 >> 2), col));
+                        for (int v2 = 0; v2 < 2; ++v2) acc[u][v2] = mfma16(fa[v2], qreg[u][ks], acc[u][v2]);
                     }
                 sched_fence();
 #pragma unroll
-                for (int hs = 0; hs < 2; ++hs)
+                for (int v2 = 0; v2 < 2; ++v2) fa[v2] = fb[v2];
+            }
+            s16x4 va[C::CT][2];
 #pragma unroll
-                    for (int ct = 0; ct < C::CT; ++ct)
-                        oacc[u][ct] = mfma16(cat(va[hs][ct][0], va[hs][ct][1]), pb[hs], oacc[u][ct]);
+            for (int ct = 0; ct < C::CT; ++ct) {
+                const int col = ct * 16 + 4 * (l16 & 3);
+                va[ct][0] = lds_tr_b(Vc + C::voff(4 * g + (l16 >> 2), col));
+                va[ct][1] = lds_tr_b(Vc + C::voff(16 + 4 * g + (l16 >> 2), col));
+            }
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u) {
+                if (!need[u]) continue;
+                const int jq = 16 * qtile[u] + l16;
+                bf16x8 pb;
+#pragma unroll
+                for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = kbi * C::KB + 16 * v2 + 4 * g + r;
+                        const float x = (t <= jq) ? acc[u][v2][r] * dec[jq - t] : 0.f;
+                        pb[4 * v2 + r] = static_cast<__bf16>(x);
+                    }
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(cat(va[ct][0], va[ct][1]), pb, oacc[u][ct]);
             }
         }
 
@@ -474,7 +491,8 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                     pend_o[u][ct][1] = pack_bf16x2((oacc[u][ct][2] - mu) * inv, (oacc[u][ct][3] - mu) * inv);
                 }
             }
-            if (C::NB == 1) __syncthreads();  // every wave has read S_old^T
+            // S_old^T was last read at this chunk's first block, before the
+            // barrier of its second block
             write_st();
         }
     };
@@ -666,12 +684,14 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
                            reinterpret_cast<uint16_t *>(wsb + m.qr), reinterpret_cast<uint16_t *>(wsb + m.kr));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    main_kernel_begin(st);
     switch (p->dk) {
     case 64: e = dispatch_bc<64>(c, a, chunk, st); break;
     case 128: e = dispatch_bc<128>(c, a, chunk, st); break;
     case 256: e = dispatch_bc<256>(c, a, chunk, st); break;
     default: e = hipErrorNotSupported;
     }
+    main_kernel_end(st);
     if (e != hipSuccess) return e;
     if (a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;

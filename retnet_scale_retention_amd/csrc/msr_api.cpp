@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 msr_status fail(msr_status s, const char *fmt, ...) {
     va_list ap;
@@ -126,9 +127,22 @@ msr_status hip_status(hipError_t e, const char *what) {
 
 }  // namespace
 
+void main_kernel_begin(hipStream_t st) {
+    if (g_ev_start) (void)hipEventRecord(g_ev_start, st);
+}
+
+void main_kernel_end(hipStream_t st) {
+    if (g_ev_stop) (void)hipEventRecord(g_ev_stop, st);
+}
+
 extern "C" {
 
 int msr_abi_version(void) { return MSR_ABI_VERSION; }
+
+void msr_set_kernel_events(void *start, void *stop) {
+    g_ev_start = static_cast<hipEvent_t>(start);
+    g_ev_stop = static_cast<hipEvent_t>(stop);
+}
 
 const char *msr_last_error(void) { return g_err; }
 
@@ -178,9 +192,12 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
     hipError_t e = launch_rotate(c, p->dtype, Q, qr, 1.f, st);
     if (e == hipSuccess) e = launch_rotate(c, p->dtype, K, kr, c.scale, st);
     // outputs first: they read state_in, which state_out may overwrite
-    if (e == hipSuccess)
+    if (e == hipSuccess) {
+        main_kernel_begin(st);
         e = launch_generic_output(c, p->dtype, p->T, qr, kr, V, O, state_in,
                                   (int64_t)p->dk * p->dv, 0, st);
+        main_kernel_end(st);
+    }
     if (e == hipSuccess && state_out)
         e = launch_generic_state(c, p->dtype, p->T, kr, V, state_in, state_out, nullptr, st);
     return hip_status(e, "generic parallel");
@@ -214,9 +231,12 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     hipError_t e = launch_rotate(c, p->dtype, Q, qr, 1.f, st);
     if (e == hipSuccess) e = launch_rotate(c, p->dtype, K, kr, c.scale, st);
     if (e == hipSuccess) e = launch_generic_state(c, p->dtype, chunk, kr, V, state_in, state_out, cs, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess) {
+        main_kernel_begin(st);
         e = launch_generic_output(c, p->dtype, chunk, qr, kr, V, O, cs,
                                   nchunks * p->dk * p->dv, (int64_t)p->dk * p->dv, st);
+        main_kernel_end(st);
+    }
     return hip_status(e, "generic chunkwise");
 }
 
@@ -233,8 +253,11 @@ msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k
     if (o == q || o == k || o == v || o == (void *)state)
         return fail(MSR_ERR_INVALID_ARG, "o must not alias q, k, v or state");
     const MsrConst c = make_const(p, 1);
-    return hip_status(launch_decode(c, p->dtype, q, k, v, o, state, static_cast<hipStream_t>(hip_stream)),
-                      "decode step");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    main_kernel_begin(st);
+    const hipError_t e = launch_decode(c, p->dtype, q, k, v, o, state, st);
+    main_kernel_end(st);
+    return hip_status(e, "decode step");
 }
 
 }  // extern "C"

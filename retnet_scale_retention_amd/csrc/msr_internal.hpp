@@ -49,3 +49,8 @@ hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void
 
 // s_out = s_in (or zeros when s_in is NULL); used for T == 0.
 hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out, hipStream_t st);
+
+// Measurement hook (msr_set_kernel_events): records the caller's events
+// around the main kernel of a call on its stream.  No-ops when unset.
+void main_kernel_begin(hipStream_t st);
+void main_kernel_end(hipStream_t st);

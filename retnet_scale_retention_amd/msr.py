@@ -24,7 +24,7 @@ STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
 EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_parallel",
-           "msr_chunkwise", "msr_recurrent_step")
+           "msr_chunkwise", "msr_recurrent_step", "msr_set_kernel_events")
 
 
 class MsrError(RuntimeError):
@@ -67,6 +67,8 @@ def load():
     lib.msr_chunkwise.restype = ctypes.c_int
     lib.msr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.msr_recurrent_step.restype = ctypes.c_int
+    lib.msr_set_kernel_events.argtypes = [vp, vp]
+    lib.msr_set_kernel_events.restype = None
     del fp
     _lib = lib
     return lib
@@ -201,3 +203,10 @@ def msr_recurrent_step(q, k, v, state, gamma, pos, *, theta=None, scale=0.0, eps
     _check(load().msr_recurrent_step(d.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
                                      _stream(q, stream)))
     return out
+
+
+def set_kernel_events(start=None, stop=None):
+    """Measurement hook: record the hipEvent handles `start` / `stop` (ints
+    or None) around the main kernel of every later call on this thread."""
+    load().msr_set_kernel_events(ctypes.c_void_p(start) if start else None,
+                                 ctypes.c_void_p(stop) if stop else None)
