@@ -15,7 +15,7 @@ already resident in HBM.  The same JSON line also reports
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -176,18 +176,19 @@ def bench_decode(torch, msr, mi, nsteps):
         "steps_per_s": 1e3 / step_ms, "tokens_per_s": w.B * 1e3 / step_ms,
         "ms_per_step": step_ms, "kernel_us": kms * 1e3,
         "hbm": {"achieved": bytes_step / (kms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": bytes_step / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": bytes_step},
+                "frac": bytes_step / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": bytes_step,
+                "traffic": traffic_record("decode_kernel")},
         "prefill_ms": prefill_ms,
     }
 
 
 def cpu_baseline(mi, chunk):
     """The oracle's chunkwise form on a bounded sample of the 7B workload:
-    16 (batch, head) pairs x 4096 tokens, scaled linearly to the full B*T*H
+    16 (batch, head) pairs x 8192 tokens, scaled linearly to the full B*T*H
     token-heads (the form's cost is linear in tokens and pairs)."""
     from oracle import oracle
     w = mi.WORKLOADS["7b"]
-    Ts, Hs = 4096, 16
+    Ts, Hs = 8192, 16
     q, k, v = mi.qkv(w, T=Ts)
     q, k, v = (x[:1, :, :Hs] for x in (q, k, v))
     g = mi.gammas(w.H)[:Hs]
@@ -198,7 +199,7 @@ def cpu_baseline(mi, chunk):
     full = w.B * w.T * w.H
     tokens_per_s = w.B * w.T / (dt * full / token_heads)
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"chunkwise form, chunk {chunk}, 16 heads x 4096 tokens of the 7B-shaped layer "
+            "sample": f"chunkwise form, chunk {chunk}, {Hs} heads x {Ts} tokens of the 7B-shaped layer "
                       f"({dt:.1f} s), scaled to B*T*H = {full} token-heads"}
 
 
@@ -211,6 +212,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run 3 plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the operator runs on a single MI355X here "
@@ -231,6 +234,13 @@ def main():
     w = r["workload"]
     dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
     cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     traffic = traffic_record("chunk_mfma_kernel")
     line = {
         "metric": "chunkwise MSR fwd tokens/s + decode steps/s; % of bf16 MFMA / HBM peak",
