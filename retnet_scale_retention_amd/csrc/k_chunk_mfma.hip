@@ -6,36 +6,45 @@
 //   S_i = gamma^b S_{i-1} + K~_i^T (V_i (.) zeta)
 //
 // Kernels, in launch order:
-//   angle_table_kernel  cos/sin of (pos0 + t) theta_i for every position
-//   rotate_qk_kernel    Q~, K~ = theta_shift(Q), theta_shift(K) as bf16, once
-//                       per token and head (bandwidth bound)
-//   chunk_mfma_kernel   the chunk recurrence, below
+//   prep_kernel         per (pair, chunk), fully parallel: rotates the chunk's
+//                       Q and K rows, computes its masked, decayed scores
+//                       P = (Q~ K~^T (.) D) s, and writes Q~, K~^T and P^T as
+//                       MFMA operand fragments
+//   chunk_mfma_kernel   the recurrence over the chunks, below
 //   gn_finalize_kernel  GroupNorm when d_v spans several slices
 //
-// Work decomposition of chunk_mfma_kernel.  One workgroup owns one (batch,
-// head) pair and one slice of W = 64 value columns for the WHOLE sequence;
-// its fp32 state slice S[dk][W] lives in MFMA accumulators for the entire
-// run, split over the waves in 16x16 tiles.  Per chunk the workgroup
-//   1. stages the chunk's K~ [b][dk], its V slice [b][W] and V (.) zeta s in
-//      LDS (bf16); each wave holds the Q~ rows of its query tiles in registers
-//      (loaded straight from memory in MFMA operand layout); all of it was
-//      prefetched into registers during the previous chunk;
-//   2. state update: S = gamma^b S + K~^T (V (.) zeta s) -- both operands are
-//      token-contiguous reads of the row-major LDS tiles, done with the gfx950
-//      LDS transpose read (ds_read_b64_tr_b16);
-//   3. per query tile of 16 rows:
-//        O^T  = (S_old^T Q~^T) (.) xi                 (S_old^T bf16 in LDS)
-//        P^T  = mask(K~ Q~^T) -- decay and scale applied in registers
-//        O^T += V^T P^T      -- P^T stays in registers: two 16x16 result
-//                              tiles form the next MFMA's B operand once the
-//                              keys are taken in the order
-//                              {4g..4g+3, 16+4g..16+4g+3} for lane group g,
-//                              and V^T is read in that same order;
-//      then GroupNorm over d_v (in-wave when W == d_v, else the slice writes
-//      its row statistics and the finalize pass normalises);
-//   4. writes S_new^T as bf16 to LDS for the next chunk's inter-chunk term.
-// Decay factors gamma^d are exp2(d log2 gamma) with d >= 0, tabulated once
-// per workgroup in LDS.
+// Fragments.  A 16x16x32 MFMA operand is 64 lanes x 8 bf16: lane 16 g + n
+// holds row n, k-indices 8 g .. 8 g + 7.  prep_kernel stores each operand the
+// chunk kernel reads from memory in exactly that order, 1 KiB per fragment,
+// so every such load is one coalesced 16-byte-per-lane read into registers:
+//   QF[pair][chunk][u][ks]  Q~, query rows 16 u.., d_k columns 32 ks..
+//                           (B operand of the inter-chunk product)
+//   KF[pair][chunk][rt][kb] (K~ zeta s)^T, d_k rows 16 rt.., tokens 32 kb..
+//                           with zeta_t s = s gamma^(b-1-t) applied
+//                           (A operand of the state update)
+//   PF[pair][chunk][u][kb]  P^T, keys 32 kb.., query columns 16 u.., keys in
+//                           the order {4g..4g+3, 16+4g..16+4g+3} of lane
+//                           group g -- the values two 16x16 result tiles of
+//                           P^T = K~ Q~^T leave in each lane
+//                           (B operand of the value product)
+//
+// chunk_mfma_kernel.  A workgroup of NW waves (4, or 8 for b = 256) owns one (batch, head) pair
+// and a slice of W = 64 value columns for the whole sequence; its fp32 state
+// slice S[d_k][W] stays in MFMA accumulators for the entire run, split over
+// the waves in 16x16 tiles.  Per chunk, behind one barrier:
+//   - the chunk's V slice is in LDS (direct global->LDS loads issued one
+//     chunk ahead into the other of two buffers);
+//   - O^T = (S_old^T Q~^T) (.) xi, with S_old^T as bf16 in LDS;
+//   - S = gamma^b S, then per 32-key block S += (K~ zeta s)^T V and
+//     O^T += V^T P^T; V and V^T come from the gfx950 LDS transpose read
+//     (ds_read_b64_tr_b16);
+//   - GroupNorm of each output row over the slice (final when W == d_v,
+//     otherwise (mean, M2) partials for gn_finalize_kernel);
+//   - S_new^T as bf16 to the other LDS state buffer.
+// Each register fragment is reloaded for a later block right after its last
+// use, so the loads have most of a chunk to land.  Every wave issues the same
+// loads in the same order each chunk, so one fixed vmcnt wait tells when the
+// next V slice has landed.
 #include "msr_device.hpp"
 #include "msr_mfma.hpp"
 
@@ -44,23 +53,26 @@ namespace {
 using namespace msr;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int W = 64;  // value columns per workgroup slice
+constexpr int W = 64;      // value columns per workgroup slice
+constexpr int FRAG = 512;  // bf16 elements per operand fragment
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS transpose read: 16 lanes each point at 4 consecutive bf16 of row
-// (base_row + j/4) -- lane i receives column (i) of the 4 rows addressed by
-// the lanes {i/4, 4 + i/4, 8 + i/4, 12 + i/4}.  With lane j addressing
-// &tile[r0 + j/4][c0 + 4 (j%4)], lane i gets tile[r0 + e][c0 + i], e = 0..3.
-__device__ __forceinline__ s16x4 lds_tr(const __bf16 *p) {
+// LDS transpose read: within each 16-lane group, lane j points at 4
+// consecutive bf16 of row r0 + j/4, columns c0 + 4 (j%4) ..; lane i then
+// receives column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 lds_tr(const void *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
 }
@@ -74,61 +86,6 @@ __device__ __forceinline__ float bf(short s) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(s)) << 16);
 }
 
-__device__ __forceinline__ bf16x8 ld_lds8(const __bf16 *p) {
-    return *reinterpret_cast<const bf16x8 *>(p);
-}
-
-template <int DK, int BC>
-struct Cfg {
-    static constexpr int KB = 32;                        // keys per LDS block (one k-step)
-    static constexpr int NB = BC / KB;                   // key blocks per chunk
-    static constexpr int NKT = BC / 16;                  // 16-token tiles per chunk
-    // waves and query tiles per wave: two tiles per wave (fragment reuse)
-    // except for the smallest chunk
-    static constexpr int NQT = NKT >= 8 ? 2 : 1;
-    static constexpr int NW = NKT / NQT;
-    static constexpr int THREADS = NW * 64;
-    static constexpr int CT = W / 16;          // state / output column tiles
-    static constexpr int NT = (DK / 16) * CT;  // state tiles per workgroup
-    static constexpr int TPW = NT / NW;        // state tiles per wave
-    static constexpr int CPW = TPW < CT ? TPW : CT;  // ... of which column tiles
-    static constexpr int RPW = TPW / CPW;            // ... and row tiles
-    static constexpr int CG = CT / CPW;              // column groups of waves
-    static constexpr int KS = DK / 32;      // k-steps over d_k
-    static constexpr int KROW = DK * 2;     // bytes per K~ / Q~ row in LDS (swizzled)
-    static constexpr int KBLK = KB * KROW;  // bytes per K~ block
-    static constexpr int VROW = W * 2;      // bytes per V row
-    static constexpr int VBLK = KB * VROW;  // bytes per V block
-    static constexpr bool QLDS = BC * DK <= 32768;   // next chunk's Q~ staged in LDS
-    static constexpr int QBLK = QLDS ? BC * KROW : 16;
-    static constexpr int SP = DK + 8;       // padded LDS row of S^T (bf16)
-    static_assert(NKT % NQT == 0 && NW <= 16, "query tiles split over waves");
-    static_assert(NT % NW == 0 && TPW >= 1, "state tiles must split evenly over waves");
-    static_assert(KBLK % 1024 == 0 && VBLK % 1024 == 0, "1 KiB direct-load units");
-    static_assert(2 * KBLK + 2 * VBLK + QBLK + W * SP * 2 + 3 * BC * 4 <= 163840, "LDS budget");
-    // XOR swizzle of the 16-byte chunks of a row: 16 consecutive rows read
-    // at one logical chunk hit 16 different bank groups
-    __device__ static int swz_k(int row) { return DK >= 128 ? (row & 15) : ((row >> 1) & 7); }
-    __device__ static int swz_v(int row) { return (row >> 1) & 7; }
-    __device__ static int koff(int row, int col) {  // byte offset of K~[row][col] (also Q~)
-        return row * KROW + ((((col >> 3) ^ swz_k(row))) << 4) + (col & 7) * 2;
-    }
-    __device__ static int voff(int row, int col) {
-        return row * VROW + ((((col >> 3) ^ swz_v(row))) << 4) + (col & 7) * 2;
-    }
-};
-
-struct ChunkArgs {
-    const uint16_t *q, *k, *v;  // Q~, K~ (already rotated), V
-    uint16_t *o;
-    const float *s_in;
-    float *s_out;
-    float2 *stats;  // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
-    int NS;         // slices per pair (dv / W)
-};
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     const bf16x2 y = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
     return __builtin_bit_cast(uint32_t, y);
@@ -138,6 +95,19 @@ __device__ __forceinline__ u32x4 ld16(const char *base, uint32_t off) {
     return *reinterpret_cast<const u32x4 *>(base + off);
 }
 
+__device__ __forceinline__ bf16x8 ldf(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48], the same bits in every lane, with
+// the gfx950 lane-swap instructions (permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second, permlane32_swap
+// the upper half of the first with the lower half of the second)
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at lds + 16 l (the LDS address is wave-uniform).
 __device__ __forceinline__ void load_lds16(const void *gptr, void *lds) {
@@ -145,9 +115,7 @@ __device__ __forceinline__ void load_lds16(const void *gptr, void *lds) {
                                      (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
-// Keeps the scheduler from moving instructions across this point: used to
-// issue the LDS fragment loads of the next k-step before the MFMAs of the
-// current one.
+// Keeps the scheduler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding)
@@ -157,25 +125,247 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ s16x4 lds_tr_b(const char *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((__attribute__((address_space(3))) char *)(p)));
+template <int DK, int BC>
+struct Cfg {
+    static constexpr int NKT = BC / 16;        // 16-token tiles per chunk
+    static constexpr int NB = BC / 32;         // 32-key blocks per chunk
+    static constexpr int KS = DK / 32;         // 32-wide k-steps over d_k
+    static constexpr int RT = DK / 16;         // 16-row tiles of d_k
+    static constexpr int NW = BC == 256 ? 8 : 4;  // waves per workgroup
+    static constexpr int THREADS = NW * 64;
+    static constexpr int NQT = NKT / NW;       // query tiles per wave
+    static constexpr int CT = W / 16;          // value column tiles
+    static constexpr int TPW = RT * CT / NW;   // 16x16 state tiles per wave
+    static constexpr int CPW = TPW < CT ? TPW : CT;  // ... in this many column tiles
+    static constexpr int RPW = TPW / CPW;            // ... and row tiles
+    static constexpr int CG = CT / CPW;              // column groups of waves
+    static constexpr int R = NB <= 4 ? NB : 1; // key blocks of K~^T / P^T fragments held in registers
+    static constexpr int KROW = DK * 2;        // bytes per K~ row in LDS (prep_kernel)
+    static constexpr int VROW = W * 2;         // bytes per V row in LDS
+    static constexpr int VTILE = BC * VROW;    // bytes of a chunk's V slice
+    static constexpr int NV = VTILE / 1024 / NW;  // direct-load units per wave per chunk
+    static constexpr int SP = DK + 8;          // padded LDS row of S^T (bf16)
+    // memory operations each wave issues per chunk after the next V slice:
+    // per block, its K~^T and P^T fragments and a share of the next chunk's
+    // Q~ fragments.  The V loads go first (during the inter-chunk product)
+    // when the count allows, else right before block KBV.
+    static constexpr int NQ = NQT * KS;
+    static constexpr int PER_BLK = RPW + NQT;
+    __host__ __device__ static constexpr int qpart0(int kb) { return kb * NQ / NB; }  // first Q~ load of block kb
+    __host__ __device__ static constexpr int after_v(int kbv) { return (NB - kbv) * PER_BLK + NQ - qpart0(kbv); }
+    __host__ __device__ static constexpr int first_kbv() {
+        int kb = 0;
+        while (kb < NB && after_v(kb) > 63) ++kb;
+        return kb;
+    }
+    static constexpr bool V_FIRST = after_v(0) <= 63;
+    static constexpr int KBV = V_FIRST ? 0 : first_kbv();
+    static constexpr int VWAIT = after_v(KBV);
+    static_assert(NQT >= 1 && RPW >= 1 && NV >= 1 && (NW / CG) * RPW == RT && CG * CPW == CT, "shape");
+    static_assert(VWAIT <= 63 && KBV < NB, "vmcnt range");
+    static_assert(2 * VTILE + 2 * W * SP * 2 + 2 * BC * 4 <= 163840, "LDS budget (chunk kernel)");
+    // query tiles of wave w: w, 2 NW - 1 - w, 2 NW + w, 4 NW - 1 - w, ... (equal causal work)
+    __device__ static int qtile(int w, int i) {
+        return (i & 1) ? 2 * NW * (i / 2 + 1) - 1 - w : 2 * NW * (i / 2) + w;
+    }
+    // XOR swizzle of the 16-byte chunks of a row: 16 consecutive rows read at
+    // one logical chunk land in different bank groups
+    __device__ static int swz_k(int row) { return DK >= 128 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static int swz_v(int row) { return (row >> 1) & 7; }
+    __device__ static int koff(int row, int col) {  // byte offset of K~[row][col]
+        return row * KROW + ((((col >> 3) ^ swz_k(row))) << 4) + (col & 7) * 2;
+    }
+    __device__ static int voff(int row, int col) {
+        return row * VROW + ((((col >> 3) ^ swz_v(row))) << 4) + (col & 7) * 2;
+    }
+};
+
+struct ChunkArgs {
+    const uint16_t *qf, *kf, *pf;  // fragments written by prep_kernel
+    const uint16_t *v;
+    uint16_t *o;
+    const float *s_in;
+    float *s_out;
+    float2 *stats;  // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
+    int NS;         // slices per pair (dv / W)
+};
+
+// Per (pair, chunk): rotation of the chunk's Q and K rows (theta_shift,
+// jsqmd.com s2: pair i of the token at position p becomes
+// (x0 c - x1 s, x1 c + x0 s) with c, s = cos, sin of p theta_i; fp32
+// arithmetic, rounded to bf16), then the chunk's scores
+//   P[j][t] = s gamma^(j-t) (q~_j . k~_t) for t <= j, else 0
+// with the decay and the causal mask applied in registers.  Writes the QF,
+// KF and PF fragments described at the top of the file.
+//
+// Rotation: thread (c8, rg) handles channels 8 c8 .. 8 c8 + 7 (4 pairs) of a
+// run of RPT consecutive rows.  The angles of the run's first row come from
+// rot_cos_sin (fp64 reduction); each next row multiplies (cos, sin) by
+// (cos theta_i, sin theta_i) -- the angle-addition formula, a few ulp of
+// drift over at most 16 rows.  Q~ goes straight to its fragments in global
+// memory, K~ of the chunk to LDS; the score products read Q~ back from the
+// fragments (visible to the workgroup after the barrier).  P^T fragments of key blocks a query tile does not reach are not written
+// (the chunk kernel loads but never uses them).
+template <int DK, int BC>
+__global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
+                                                   const uint16_t *__restrict__ k, uint16_t *__restrict__ qf,
+                                                   uint16_t *__restrict__ kf, uint16_t *__restrict__ pf) {
+    using C = Cfg<DK, BC>;
+    constexpr int NT = 512, PW = NT / 64;  // threads, waves
+    constexpr int C8 = DK / 8;             // 16-byte channel groups per row
+    constexpr int RG = NT / C8;            // row runs
+    constexpr int RPT = BC / RG;           // rows per run
+    static_assert(RPT >= 1 && RG * RPT == BC, "row runs");
+    static_assert(BC * C::KROW + BC * 4 <= 163840, "LDS budget (prep kernel)");
+    __shared__ __attribute__((aligned(16))) char Ks[BC * C::KROW];  // K~, swizzled rows
+    __shared__ float dec[BC], zet[BC];                                // s gamma^d, s gamma^(BC-1-t)
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int nch = c.T / BC;
+    const int pair = blockIdx.x / nch, ci = blockIdx.x % nch;
+    const int b = pair / c.H, h = pair % c.H;
+    const float lg = c.log2g[h];
+    for (int t = tid; t < BC; t += NT) {
+        dec[t] = c.scale * exp2f((float)t * lg);
+        zet[t] = c.scale * exp2f((float)(BC - 1 - t) * lg);
+    }
+
+    const uint32_t rowQK = (uint32_t)c.H * DK * 2;  // bytes between tokens of Q, K
+    const size_t base = (((size_t)b * c.T + (size_t)ci * BC) * c.H + h) * DK;
+    const char *qrow = reinterpret_cast<const char *>(q + base);
+    const char *krow = reinterpret_cast<const char *>(k + base);
+
+    uint16_t *qfo = qf + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG);
+    {  // ---- rotation: Q~ to its fragments, K~ into LDS
+        const int c8 = tid % C8, r0 = (tid / C8) * RPT;
+        u32x4 xq[RPT], xk[RPT];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            xq[j] = ld16(qrow, (uint32_t)(r0 + j) * rowQK + c8 * 16);
+            xk[j] = ld16(krow, (uint32_t)(r0 + j) * rowQK + c8 * 16);
+        }
+        float cc[4] = {1.f, 1.f, 1.f, 1.f}, ss[4] = {0.f, 0.f, 0.f, 0.f}, c1[4], s1[4];
+        const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
+        if (rot) {
+            const int64_t p0 = c.pos0 + (int64_t)ci * BC + r0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float th = c.theta[4 * c8 + i];
+                rot_cos_sin(p0, th, cc[i], ss[i]);
+                rot_cos_sin(1, th, c1[i], s1[i]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            u32x4 yq, yk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x0 = __uint_as_float(xq[j][i] << 16), x1 = __uint_as_float(xq[j][i] & 0xffff0000u);
+                yq[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
+                x0 = __uint_as_float(xk[j][i] << 16);
+                x1 = __uint_as_float(xk[j][i] & 0xffff0000u);
+                yk[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
+            }
+            // fragment (u, ks) = (row / 16, c8 / 4), lane 16 (c8 % 4) + row % 16
+            const int row = r0 + j;
+            *reinterpret_cast<u32x4 *>(qfo + (size_t)((row >> 4) * C::KS + (c8 >> 2)) * FRAG +
+                                       (16 * (c8 & 3) + (row & 15)) * 8) = rot ? yq : xq[j];
+            *reinterpret_cast<u32x4 *>(Ks + C::koff(row, c8 * 8)) = rot ? yk : xk[j];
+            if (rot && j + 1 < RPT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float cn = cc[i] * c1[i] - ss[i] * s1[i];
+                    ss[i] = ss[i] * c1[i] + cc[i] * s1[i];
+                    cc[i] = cn;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- (K~ zeta s)^T fragments: lane (n, g) of fragment (rt, kb) holds
+    // K~[t][16 rt + n] s gamma^(BC-1-t) for t = 32 kb + 8 g + e
+    uint16_t *kfo = kf + (size_t)blockIdx.x * (C::RT * C::NB * FRAG) + lane * 8;
+    for (int f = w; f < C::RT * C::NB; f += PW) {
+        const int rt = f / C::NB, kb = f % C::NB;
+        const int row = 32 * kb + 8 * g + (l16 >> 2), col = 16 * rt + 4 * (l16 & 3);
+        const s16x4 lo = lds_tr(Ks + C::koff(row, col)), hi = lds_tr(Ks + C::koff(row + 4, col));
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = static_cast<__bf16>(bf(lo[e]) * zet[32 * kb + 8 * g + e]);
+            x[4 + e] = static_cast<__bf16>(bf(hi[e]) * zet[32 * kb + 8 * g + 4 + e]);
+        }
+        *reinterpret_cast<bf16x8 *>(kfo + (size_t)f * FRAG) = x;
+    }
+
+    // ---- P^T = K~ Q~^T per 32-key block, masked, decayed, scaled; wave w
+    // takes query tiles w and NKT - 1 - w (or w alone when NKT <= 8)
+    constexpr int NU = C::NKT > PW ? 2 : 1;
+    if (w >= C::NKT) return;
+    int qt[NU];
+    qt[0] = w;
+    if (NU == 2) qt[NU - 1] = C::NKT - 1 - w;
+    uint16_t *pfo = pf + (size_t)blockIdx.x * (C::NKT * C::NB * FRAG) + lane * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb) {
+        bool nd[NU];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            nd[u] = 32 * kb <= 16 * qt[u] + 15;
+            any = any || nd[u];
+        }
+        if (!any) continue;
+        f32x4 acc[NU][2];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            bf16x8 ka[2], qb[NU];
+#pragma unroll
+            for (int v2 = 0; v2 < 2; ++v2)
+                ka[v2] = *reinterpret_cast<const bf16x8 *>(Ks + C::koff(32 * kb + 16 * v2 + l16, 32 * ks + 8 * g));
+#pragma unroll
+            for (int u = 0; u < NU; ++u) qb[u] = ldf(qfo + (size_t)(qt[u] * C::KS + ks) * FRAG + lane * 8);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                if (nd[u]) {
+#pragma unroll
+                    for (int v2 = 0; v2 < 2; ++v2) acc[u][v2] = mfma16(ka[v2], qb[u], acc[u][v2]);
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (!nd[u]) continue;
+            const int jq = 16 * qt[u] + l16;
+            bf16x8 pb;
+#pragma unroll
+            for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 32 * kb + 16 * v2 + 4 * g + r;
+                    pb[4 * v2 + r] = static_cast<__bf16>((t <= jq) ? acc[u][v2][r] * dec[jq - t] : 0.f);
+                }
+            *reinterpret_cast<bf16x8 *>(pfo + (size_t)(qt[u] * C::NB + kb) * FRAG) = pb;
+        }
+    }
 }
 
 template <int DK, int BC>
 __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
-    // separate LDS objects for the two block buffers and the Q~ tile, so the
-    // compiler can tell the direct loads into one from reads of another
-    __shared__ __attribute__((aligned(16))) char Kb0[C::KBLK], Kb1[C::KBLK];
-    __shared__ __attribute__((aligned(16))) char Vb0[C::VBLK], Vb1[C::VBLK];
-    __shared__ __attribute__((aligned(16))) char Qs[C::QBLK];
-    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_old^T
-    __shared__ float dec[BC], xi[BC], zet[BC];  // s gamma^d, gamma^(j+1), s gamma^(BC-1-t)
+    // separate LDS objects for the two V buffers, so the compiler can tell the
+    // direct loads into one from reads of the other
+    __shared__ __attribute__((aligned(16))) char Vb0[C::VTILE], Vb1[C::VTILE];
+    __shared__ __attribute__((aligned(16))) __bf16 St0[W * C::SP], St1[W * C::SP];  // S_old^T
+    __shared__ float xi[BC];  // gamma^(j+1)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     // workgroup -> (pair, slice): the slices of one pair get ids equal mod 8,
-    // i.e. run on the same XCD and share its L2 for the Q~ and K~ chunks.
+    // i.e. run on the same XCD and share its L2 for the pair's fragments
     const int npairs = c.B * c.H;
     int pair, slice;
     {
@@ -192,59 +382,62 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * W;
     const float lg = c.log2g[h];
-
-    for (int t = tid; t < BC; t += C::THREADS) {
-        dec[t] = c.scale * exp2f((float)t * lg);
-        xi[t] = exp2f((float)(t + 1) * lg);
-        zet[t] = c.scale * exp2f((float)(BC - 1 - t) * lg);
-    }
+    for (int t = tid; t < BC; t += C::THREADS) xi[t] = exp2f((float)(t + 1) * lg);
     const float gb = exp2f((float)BC * lg);
 
-    // uniform bases of this pair's rows; per-thread byte offsets fit 32 bits
-    const uint32_t rowQK = (uint32_t)c.H * DK * 2;        // bytes between tokens of Q~, K~
-    const uint32_t rowV = (uint32_t)c.H * c.dv * 2;       // bytes between tokens of V
-    const char *qb = reinterpret_cast<const char *>(a.q + ((size_t)b * c.T * c.H + h) * DK);
-    const char *kb = reinterpret_cast<const char *>(a.k + ((size_t)b * c.T * c.H + h) * DK);
+    const int nch = c.T / BC;
+    const size_t pc0 = (size_t)pair * nch;  // (pair, chunk 0) index of the fragments
+    const uint16_t *qfb = a.qf + pc0 * (C::NKT * C::KS * FRAG) + lane * 8;
+    const uint16_t *kfb = a.kf + pc0 * (C::RT * C::NB * FRAG) + lane * 8;
+    const uint16_t *pfb = a.pf + pc0 * (C::NKT * C::NB * FRAG) + lane * 8;
+    const uint32_t rowV = (uint32_t)c.H * c.dv * 2;  // bytes between tokens of V
     const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
 
-    // direct loads of 1 KiB units: unit u of a [rows][row bytes] tile whose
-    // row r starts at global byte base + r * rstride; units go round-robin
-    // over the waves
-    auto dma_k = [&](const char *gbase, int tok0, char *dst, int nbytes) {
-        for (int u = w; u < nbytes / 1024; u += C::NW) {
-            const int byte = u * 1024 + lane * 16;
-            const int row = byte / C::KROW, phys = (byte % C::KROW) >> 4;
-            load_lds16(gbase + (uint32_t)(tok0 + row) * rowQK + (phys ^ C::swz_k(row)) * 16, dst + u * 1024);
-        }
-    };
-    auto dma_v = [&](int tok0, char *dst) {
-        for (int u = w; u < C::VBLK / 1024; u += C::NW) {
-            const int byte = u * 1024 + lane * 16;
-            const int row = byte / C::VROW, phys = (byte % C::VROW) >> 4;
-            load_lds16(vb + (uint32_t)(tok0 + row) * rowV + (phys ^ C::swz_v(row)) * 16, dst + u * 1024);
-        }
-    };
+    int qt[C::NQT];
+#pragma unroll
+    for (int i = 0; i < C::NQT; ++i) qt[i] = C::qtile(w, i);
+    // state tiles of this wave: row tiles rbase.., column tiles cbase..
+    const int rbase = (w / C::CG) * C::RPW, cbase = (w % C::CG) * C::CPW;
 
-    // query tiles of this wave: w and, with two, NKT-1-w (balances the causal work)
-    int qtile[C::NQT];
-    qtile[0] = w;
-    if (C::NQT == 2) qtile[C::NQT - 1] = C::NKT - 1 - w;
-    bf16x8 qreg[C::NQT][C::KS];  // this chunk's Q~ rows in MFMA operand layout
-    auto take_q = [&](int t0) {
+    // ---- loads; indices past the last chunk are clamped to it, so every
+    // wave issues the same operations every chunk
+    auto dma_v_unit = [&](int ci, int i, char *dst) {
+        ci = ci < nch ? ci : nch - 1;
+        const int unit = i * C::NW + w;
+        const int byte = unit * 1024 + lane * 16;
+        const int row = byte / C::VROW, phys = (byte % C::VROW) >> 4;
+        load_lds16(vb + (uint32_t)(ci * BC + row) * rowV + (phys ^ C::swz_v(row)) * 16, dst + unit * 1024);
+    };
+    auto dma_v = [&](int ci, char *dst) {
+#pragma unroll
+        for (int i = 0; i < C::NV; ++i) dma_v_unit(ci, i, dst);
+    };
+    bf16x8 qr[C::NQT][C::KS];   // Q~ fragments of the current chunk
+    bf16x8 kr[C::RPW][C::R];    // K~^T fragments, slot kb % R
+    bf16x8 pr[C::NQT][C::R];    // P^T fragments, slot kb % R
+    // Q~ fragments f0 .. f1 - 1 (f = u KS + ks) of chunk ci
+    auto load_q = [&](int ci, int f0, int f1) {
+        ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+        for (int f = 0; f < C::NQ; ++f)
+            if (f >= f0 && f < f1)
+                qr[f / C::KS][f % C::KS] = ldf(qfb + ((size_t)(ci * C::NKT + qt[f / C::KS]) * C::KS + f % C::KS) * FRAG);
+    };
+    // K~^T and P^T fragments of block kb of chunk ci into slot kb % R
+    auto load_kp_k = [&](int ci, int kb) {
+        ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+        for (int rt = 0; rt < C::RPW; ++rt)
+            kr[rt][kb % C::R] = ldf(kfb + ((size_t)(ci * C::RT + rbase + rt) * C::NB + kb) * FRAG);
+    };
+    auto load_kp_p = [&](int ci, int kb) {
+        ci = ci < nch ? ci : nch - 1;
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u)
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const int row = 16 * qtile[u] + l16, col = 32 * ks + 8 * g;
-                if constexpr (C::QLDS)
-                    qreg[u][ks] = *reinterpret_cast<const bf16x8 *>(Qs + C::koff(row, col));
-                else
-                    qreg[u][ks] = __builtin_bit_cast(bf16x8, ld16(qb, (uint32_t)(t0 + row) * rowQK + col * 2));
-            }
+            pr[u][kb % C::R] = ldf(pfb + ((size_t)(ci * C::NKT + qt[u]) * C::NB + kb) * FRAG);
     };
 
-    // ---- state tiles of this wave: rows (rg*RPW + rt)*16 + 4g + r, cols (cg*CPW + ct)*16 + l16
-    const int cgw = w % C::CG, rgw = w / C::CG;
+    // ---- state tiles: d_k rows (rbase + rt) 16 + 4 g + r, columns (cbase + ct) 16 + l16
     f32x4 S[C::RPW][C::CPW];
     const size_t sbase = (size_t)pair * DK * c.dv + col0;
 #pragma unroll
@@ -253,18 +446,15 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = (rgw * C::RPW + rt) * 16 + 4 * g + r;
-                const int col = (cgw * C::CPW + ct) * 16 + l16;
+                const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
                 S[rt][ct][r] = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
             }
-    auto write_st = [&]() {
+    auto write_st = [&](__bf16 *St) {
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
             for (int ct = 0; ct < C::CPW; ++ct) {
-                const int row = (rgw * C::RPW + rt) * 16 + 4 * g;
-                const int col = (cgw * C::CPW + ct) * 16 + l16;
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const int row = (rbase + rt) * 16 + 4 * g, col = (cbase + ct) * 16 + l16;
                 bf16x4 v4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v4[r] = static_cast<__bf16>(S[rt][ct][r]);
@@ -272,235 +462,198 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             }
     };
 
-    // finished, not yet stored outputs of the previous chunk
+    // finished outputs of the previous chunk, stored during the next chunk.
+    // Before the first chunk they hold zeros for chunk 0's rows, which the
+    // real values overwrite later (stores of one wave to one address stay in
+    // order), so that every chunk issues the same stores.
     uint32_t pend_o[C::NQT][C::CT][2];
     size_t pend_row[C::NQT];
     float2 pend_stat[C::NQT];
+#pragma unroll
+    for (int u = 0; u < C::NQT; ++u) {
+        pend_row[u] = ((size_t)b * c.T + 16 * qt[u] + l16) * c.H + h;
+        pend_stat[u] = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
+    }
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    auto flush_u = [&](int u) {
+        uint16_t *dst = a.o + pend_row[u] * c.dv + col0 + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) {
+            const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
+            *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+        }
+        if (stats_out && g == 0) a.stats[pend_row[u] * a.NS + slice] = pend_stat[u];
+    };
     auto flush = [&]() {
 #pragma unroll
-        for (int u = 0; u < C::NQT; ++u) {
-            uint16_t *dst = a.o + pend_row[u] * c.dv + col0 + 4 * g;
-#pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
-                *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
-            }
-            if (stats_out && g == 0) a.stats[pend_row[u] * a.NS + slice] = pend_stat[u];
-        }
+        for (int u = 0; u < C::NQT; ++u) flush_u(u);
     };
 
-    const int nchunks = c.T / BC;
-    const int nblocks = nchunks * C::NB;
-    write_st();
-    if (nblocks > 0) {
-        if constexpr (C::QLDS) dma_k(qb, 0, Qs, C::QBLK);
-        dma_k(kb, 0, Kb0, C::KBLK);
+    write_st(St0);
+    if (nch > 0) {
         dma_v(0, Vb0);
+        load_q(0, 0, C::NQ);
+#pragma unroll
+        for (int kb = 0; kb < C::R; ++kb) {
+            load_kp_k(0, kb);
+            load_kp_p(0, kb);
+        }
     }
 
     f32x4 oacc[C::NQT][C::CT];
-    // one key block: compute on (Kc, Vc) while the next block streams into (Kn, Vn)
-    auto step = [&](int blk, const char *Kc, const char *Vc, char *Kn, char *Vn) {
-        const int ci = blk / C::NB, kbi = blk % C::NB;
+    auto chunk = [&](int ci, const char *Vc, char *Vn, const __bf16 *Sc, __bf16 *Sn) {
         const int t0 = ci * BC;
-        // this block's direct loads (issued one step ago) are complete; the
-        // Q~ tile of the next chunk, issued last in the previous step, may
-        // still be in flight
-        if (kbi == 1 && C::QLDS && ci + 1 < nchunks)
-            wait_vm<0>();  // (nothing newer to spare at this point)
-        __builtin_amdgcn_s_waitcnt(0);
+        // this chunk's V slice has landed once at most VWAIT newer operations
+        // are outstanding (the prologue issued fewer: wait for all)
+        if (ci == 0)
+            wait_vm<0>();
+        else
+            wait_vm<C::VWAIT>();
         __syncthreads();
-        if (kbi == 0) {
-            take_q(t0);
-            if (ci > 0) flush();  // previous chunk's outputs
-        }
-        if (blk + 1 < nblocks) {
-            dma_k(kb, (blk + 1) * C::KB, Kn, C::KBLK);
-            dma_v((blk + 1) * C::KB, Vn);
-        }
-        if (kbi == 0) {
-            // ---- O^T = (S_old^T Q~^T) xi for every query tile, then gamma^b S
+
+        // ---- O^T = (S_old^T Q~^T) xi.  After the MFMAs of k-step ks, memory
+        // operation ks of [previous outputs of tile 0..NQT-1, next V units]
+        // is issued (the rest after the loop): stores first, then V.
+        constexpr int NOPS = C::NQT + (C::V_FIRST ? C::NV : 0);
+        auto op = [&](int i) {
+            if (i < C::NQT) {
+                flush_u(i);
+            } else {
+                dma_v_unit(ci + 1, i - C::NQT, Vn);
+            }
+        };
+        {
             bf16x8 fa[C::CT], fb[C::CT];
 #pragma unroll
             for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) fa[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 8 * g);
+            for (int ct = 0; ct < C::CT; ++ct)
+                fa[ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 8 * g);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 if (ks + 1 < C::KS) {
 #pragma unroll
                     for (int ct = 0; ct < C::CT; ++ct)
-                        fb[ct] = ld_lds8(St + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
+                        fb[ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
                 }
                 sched_fence();
 #pragma unroll
                 for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(fa[ct], qreg[u][ks], oacc[u][ct]);
+                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(fa[ct], qr[u][ks], oacc[u][ct]);
+                sched_fence();
+                if (ks < NOPS) op(ks);
                 sched_fence();
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) fa[ct] = fb[ct];
             }
 #pragma unroll
+            for (int i = C::KS; i < NOPS; ++i) op(i);
+            sched_fence();
+#pragma unroll
             for (int u = 0; u < C::NQT; ++u) {
-                const float x = xi[16 * qtile[u] + l16];
+                const float x = xi[16 * qt[u] + l16];
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
             }
-#pragma unroll
-            for (int rt = 0; rt < C::RPW; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
         }
-        // the next chunk's Q~ tile may be overwritten once every wave has
-        // taken this chunk's rows (they all passed this step's barrier)
-        if (C::QLDS && kbi == 1 && ci + 1 < nchunks) dma_k(qb, t0 + BC, Qs, C::QBLK);
+#pragma unroll
+        for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
 
-        // ---- state update with this block's 32 tokens: S += K~^T (V zeta s)
-        {
-            const int tb = 8 * g;  // first token (within the block) of this lane group
-            s16x4 vr[C::CPW][2], kr[C::RPW][2];
+        // ---- per 32-key block: state update and value product
 #pragma unroll
-            for (int ct = 0; ct < C::CPW; ++ct) {
-                const int col = (cgw * C::CPW + ct) * 16 + 4 * (l16 & 3);
-                vr[ct][0] = lds_tr_b(Vc + C::voff(tb + (l16 >> 2), col));
-                vr[ct][1] = lds_tr_b(Vc + C::voff(tb + 4 + (l16 >> 2), col));
+        for (int kb = 0; kb < C::NB; ++kb) {
+            if (!C::V_FIRST && kb == C::KBV) {
+                sched_fence();
+                dma_v(ci + 1, Vn);
+                sched_fence();
             }
+            // the block R ahead (in this chunk or the next) reuses this slot
+            const int nb = kb + C::R;
+            const int ci2 = ci + nb / C::NB, kb2 = nb % C::NB;
+            {  // S += (K~ zeta s)^T V
+                const int tb = 32 * kb + 8 * g;
+                bf16x8 bv[C::CPW];
 #pragma unroll
-            for (int rt = 0; rt < C::RPW; ++rt) {
-                const int col = (rgw * C::RPW + rt) * 16 + 4 * (l16 & 3);
-                kr[rt][0] = lds_tr_b(Kc + C::koff(tb + (l16 >> 2), col));
-                kr[rt][1] = lds_tr_b(Kc + C::koff(tb + 4 + (l16 >> 2), col));
-            }
-            float z[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = zet[kbi * C::KB + tb + e];
-            bf16x8 bv[C::CPW];
-#pragma unroll
-            for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bv[ct][e] = static_cast<__bf16>(bf(vr[ct][0][e]) * z[e]);
-                    bv[ct][4 + e] = static_cast<__bf16>(bf(vr[ct][1][e]) * z[4 + e]);
+                for (int ct = 0; ct < C::CPW; ++ct) {
+                    const int col = (cbase + ct) * 16 + 4 * (l16 & 3);
+                    bv[ct] = cat(lds_tr(Vc + C::voff(tb + (l16 >> 2), col)), lds_tr(Vc + C::voff(tb + 4 + (l16 >> 2), col)));
                 }
 #pragma unroll
-            for (int rt = 0; rt < C::RPW; ++rt) {
-                const bf16x8 ak = cat(kr[rt][0], kr[rt][1]);
+                for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(ak, bv[ct], S[rt][ct]);
+                    for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(kr[rt][kb % C::R], bv[ct], S[rt][ct]);
             }
+            sched_fence();
+            load_kp_k(ci2, kb2);
+            sched_fence();
+            {  // O^T += V^T P^T for the query tiles that reach this block
+                s16x4 va[C::CT][2];
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) {
+                    const int col = ct * 16 + 4 * (l16 & 3);
+                    va[ct][0] = lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col));
+                    va[ct][1] = lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col));
+                }
+#pragma unroll
+                for (int u = 0; u < C::NQT; ++u) {
+                    if (!(32 * kb <= 16 * qt[u] + 15)) continue;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        oacc[u][ct] = mfma16(cat(va[ct][0], va[ct][1]), pr[u][kb % C::R], oacc[u][ct]);
+                }
+            }
+            sched_fence();
+            load_kp_p(ci2, kb2);
+            load_q(ci + 1, C::qpart0(kb), C::qpart0(kb + 1));
+            sched_fence();
         }
 
-        // ---- intra-chunk part with this block's two 16-key tiles for the
-        // query tiles that reach them (wave-uniform tests): P^T tiles with
-        // decay, scale and causal mask in registers, packed as B operands,
-        // then O^T += V^T P^T
-        bool need[C::NQT];
-        bool any = false;
+        // ---- GroupNorm over each row (lanes l16, l16+16, +32, +48 share a query)
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u) {
-            need[u] = kbi * C::KB <= 16 * qtile[u] + 15;
-            any = any || need[u];
-        }
-        if (any) {
-            f32x4 acc[C::NQT][2];
-#pragma unroll
-            for (int u = 0; u < C::NQT; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int v2 = 0; v2 < 2; ++v2)
-                fa[v2] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v2 + l16, 8 * g));
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                if (ks + 1 < C::KS) {
-#pragma unroll
-                    for (int v2 = 0; v2 < 2; ++v2)
-                        fb[v2] = *reinterpret_cast<const bf16x8 *>(Kc + C::koff(16 * v2 + l16, 32 * (ks + 1) + 8 * g));
-                }
-                sched_fence();
-#pragma unroll
-                for (int u = 0; u < C::NQT; ++u)
-                    if (need[u]) {
-#pragma unroll
-                        for (int v2 = 0; v2 < 2; ++v2) acc[u][v2] = mfma16(fa[v2], qreg[u][ks], acc[u][v2]);
-                    }
-                sched_fence();
-#pragma unroll
-                for (int v2 = 0; v2 < 2; ++v2) fa[v2] = fb[v2];
-            }
-            s16x4 va[C::CT][2];
-#pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                const int col = ct * 16 + 4 * (l16 & 3);
-                va[ct][0] = lds_tr_b(Vc + C::voff(4 * g + (l16 >> 2), col));
-                va[ct][1] = lds_tr_b(Vc + C::voff(16 + 4 * g + (l16 >> 2), col));
-            }
-#pragma unroll
-            for (int u = 0; u < C::NQT; ++u) {
-                if (!need[u]) continue;
-                const int jq = 16 * qtile[u] + l16;
-                bf16x8 pb;
-#pragma unroll
-                for (int v2 = 0; v2 < 2; ++v2)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = kbi * C::KB + 16 * v2 + 4 * g + r;
-                        const float x = (t <= jq) ? acc[u][v2][r] * dec[jq - t] : 0.f;
-                        pb[4 * v2 + r] = static_cast<__bf16>(x);
-                    }
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(cat(va[ct][0], va[ct][1]), pb, oacc[u][ct]);
-            }
-        }
-
-        if (kbi == C::NB - 1) {
-            // ---- GroupNorm over each row (lanes l16, l16+16, +32, +48 share a query)
-#pragma unroll
-            for (int u = 0; u < C::NQT; ++u) {
-                const int jq = 16 * qtile[u] + l16;
+            const int jq = 16 * qt[u] + l16;
+            pend_row[u] = ((size_t)b * c.T + t0 + jq) * c.H + h;
+            if (norm_here || stats_out) {
                 float sum = 0.f;
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct)
-                    sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
-                sum += __shfl_xor(sum, 16, 64);
-                sum += __shfl_xor(sum, 32, 64);
-                const float mean = sum * (1.f / W);
+                for (int ct = 0; ct < C::CT; ++ct) sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
+                const float mean = sum_lane_groups(sum) * (1.f / W);
                 float m2 = 0.f;
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) m2 += (oacc[u][ct][r] - mean) * (oacc[u][ct][r] - mean);
-                m2 += __shfl_xor(m2, 16, 64);
-                m2 += __shfl_xor(m2, 32, 64);
-                float mu = 0.f, inv = 1.f;
-                if (a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
-                    mu = mean;
-                    inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
-                }
-                // stored one chunk later (flush), so that waiting for the next
-                // blocks' loads does not also wait for these stores
-                pend_row[u] = ((size_t)b * c.T + t0 + jq) * c.H + h;
+                m2 = sum_lane_groups(m2);
                 pend_stat[u] = make_float2(mean, m2);
+                if (norm_here) {
+                    const float inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) {
-                    pend_o[u][ct][0] = pack_bf16x2((oacc[u][ct][0] - mu) * inv, (oacc[u][ct][1] - mu) * inv);
-                    pend_o[u][ct][1] = pack_bf16x2((oacc[u][ct][2] - mu) * inv, (oacc[u][ct][3] - mu) * inv);
+                    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) oacc[u][ct][r] = (oacc[u][ct][r] - mean) * inv;
                 }
             }
-            // S_old^T was last read at this chunk's first block, before the
-            // barrier of its second block
-            write_st();
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct) {
+                pend_o[u][ct][0] = pack_bf16x2(oacc[u][ct][0], oacc[u][ct][1]);
+                pend_o[u][ct][1] = pack_bf16x2(oacc[u][ct][2], oacc[u][ct][3]);
+            }
         }
+        write_st(Sn);
     };
-    for (int blk = 0; blk < nblocks; blk += 2) {
-        step(blk, Kb0, Vb0, Kb1, Vb1);
-        if (blk + 1 < nblocks) step(blk + 1, Kb1, Vb1, Kb0, Vb0);
+    for (int ci = 0; ci < nch; ci += 2) {
+        chunk(ci, Vb0, Vb1, St0, St1);
+        if (ci + 1 < nch) chunk(ci + 1, Vb1, Vb0, St1, St0);
     }
-    if (nchunks > 0) flush();
+    if (nch > 0) flush();
 
     if (a.s_out) {
 #pragma unroll
@@ -509,128 +662,106 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = (rgw * C::RPW + rt) * 16 + 4 * g + r;
-                    const int col = (cgw * C::CPW + ct) * 16 + l16;
+                    const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
                     a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r];
                 }
     }
+    // the clamped loads of the last chunk may still be in flight
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
-// cos/sin table of (pos0 + t) * theta_i, [T][dk/2] float2.
-__global__ void angle_table_kernel(MsrConst c, float2 *cs) {
-    const int half = c.dk / 2;
-    const size_t n = (size_t)c.T * half;
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const int i = (int)(e % half);
-        const int64_t t = (int64_t)(e / half);
-        float co, si;
-        rot_cos_sin(c.pos0 + t, c.theta[i], co, si);
-        cs[e] = make_float2(co, si);
-    }
-}
-
-// theta_shift of Q and K into bf16 copies, once per token and head: pair i
-// of the token at position pos0 + t becomes (x0 c - x1 s, x1 c + x0 s) with
-// (c, s) from the angle table; fp32 arithmetic.  8 channels per thread.
-__global__ void rotate_qk_kernel(MsrConst c, const float2 *__restrict__ cs,
-                                 const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                 uint16_t *__restrict__ qr, uint16_t *__restrict__ kr) {
-    const int p8 = c.dk / 8;
-    const size_t n = (size_t)c.B * c.T * c.H * p8;
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const int d8 = (int)(e % p8);
-        const size_t row = e / p8;  // (b * T + t) * H + h
-        const int t = (int)((row / c.H) % c.T);
-        const float4 *cp = reinterpret_cast<const float4 *>(cs + (size_t)t * (c.dk / 2) + 4 * d8);
-        const float4 c01 = cp[0], c23 = cp[1];
-        const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
-        const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
-        const u32x4 uq = reinterpret_cast<const u32x4 *>(q)[e];
-        const u32x4 uk = reinterpret_cast<const u32x4 *>(k)[e];
-        u32x4 oq, ok;
+// GroupNorm of rows whose slices wrote (mean, M2) statistics over W values
+// each: the row's mean is the mean of the slice means and its M2 the sum of
+// the slice M2 plus W (slice mean - row mean)^2 (the pairwise-update formula
+// of Chan, Golub and LeVeque for equal counts).  A thread normalises 32
+// values of one row in place (four 16-byte pieces, d_v / 32 threads per row)
+// and combines that row's statistics itself; O is streamed with
+// non-temporal loads and stores.
+__global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, const float2 *__restrict__ stats,
+                                                          uint16_t *__restrict__ o, size_t rows) {
+    const int tpr = c.dv / 32;  // threads per row
+    const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const size_t row = gid / tpr;
+    const int j = (int)(gid % tpr);
+    if (row >= rows) return;
+    u32x4 *p = reinterpret_cast<u32x4 *>(o + row * c.dv) + j;
+    u32x4 u[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x0 = __uint_as_float(uq[i] << 16), x1 = __uint_as_float(uq[i] & 0xffff0000u);
-            oq[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
-            x0 = __uint_as_float(uk[i] << 16);
-            x1 = __uint_as_float(uk[i] & 0xffff0000u);
-            ok[i] = pack_bf16x2(x0 * cc[i] - x1 * ss[i], x1 * cc[i] + x0 * ss[i]);
-        }
-        reinterpret_cast<u32x4 *>(qr)[e] = oq;
-        reinterpret_cast<u32x4 *>(kr)[e] = ok;
-    }
-}
-
-// GroupNorm of rows whose slices wrote (mean, M2) statistics: combines the
-// NS slice statistics (Chan, Golub and LeVeque's pairwise update) once per
-// row, then normalises the row's d_v values in place, 8 values (16 bytes)
-// per thread.  A block of 256 threads covers RB = 256 / (d_v / 8) rows.
-__global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, const float2 *stats,
-                                                          uint16_t *o, size_t rows) {
-    __shared__ float2 mi[256];
-    const int tpr = c.dv / 8;          // threads per row
-    const int RB = 256 / tpr;          // rows per block
-    const size_t row0 = blockIdx.x * (size_t)RB;
-    if (threadIdx.x < RB && row0 + threadIdx.x < rows) {
-        const size_t row = row0 + threadIdx.x;
-        float n = 0.f, mean = 0.f, m2 = 0.f;
-        for (int s = 0; s < NS; ++s) {
-            const float2 st = stats[row * NS + s];
-            const float nb = (float)W, nn = n + nb;
-            const float d = st.x - mean;
-            mean += d * (nb / nn);
-            m2 += st.y + d * d * (n * nb / nn);
-            n = nn;
-        }
-        mi[threadIdx.x] = make_float2(mean, 1.f / sqrtf(m2 / n + c.eps));
-    }
-    __syncthreads();
-    const int r = threadIdx.x / tpr, j = threadIdx.x % tpr;
-    if (r >= RB || row0 + r >= rows) return;
-    const float mean = mi[r].x, inv = mi[r].y;
-    u32x4 *p = reinterpret_cast<u32x4 *>(o + (row0 + r) * c.dv) + j;
-    u32x4 u = *p;
+    for (int i = 0; i < 4; ++i) u[i] = __builtin_nontemporal_load(p + i * tpr);
+    const float2 *st = stats + row * NS;
+    float2 sv[MSR_MAX_DV / W];
+    float mean = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        u[i] = pack_bf16x2((__uint_as_float(u[i] << 16) - mean) * inv,
-                           (__uint_as_float(u[i] & 0xffff0000u) - mean) * inv);
-    *p = u;
+    for (int s = 0; s < MSR_MAX_DV / W; ++s)
+        if (s < NS) {
+            sv[s] = st[s];
+            mean += sv[s].x;
+        }
+    mean /= (float)NS;
+    float m2 = 0.f;
+#pragma unroll
+    for (int s = 0; s < MSR_MAX_DV / W; ++s)
+        if (s < NS) {
+            const float d = sv[s].x - mean;
+            m2 += sv[s].y + (float)W * d * d;
+        }
+    const float inv = 1.f / sqrtf(m2 / (float)c.dv + c.eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = pack_bf16x2((__uint_as_float(u[i][e] << 16) - mean) * inv,
+                               (__uint_as_float(u[i][e] & 0xffff0000u) - mean) * inv);
+        __builtin_nontemporal_store(y, p + i * tpr);
+    }
 }
 
 template <int DK, int BC>
-hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, hipStream_t st) {
+hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, hipStream_t st) {
+    const int npairs = c.B * c.H;
+    auto pk = prep_kernel<DK, BC>;
     using C = Cfg<DK, BC>;
-    auto kern = chunk_mfma_kernel<DK, BC>;
-    const int grid = c.B * c.H * a.NS;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), 0, st, c, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(512), 0, st, c, static_cast<const uint16_t *>(Q),
+                       static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
+                       const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    main_kernel_begin(st);
+    auto ck = chunk_mfma_kernel<DK, BC>;
+    hipLaunchKernelGGL(ck, dim3(npairs * a.NS), dim3(C::THREADS), 0, st, c, a);
+    e = hipGetLastError();
+    main_kernel_end(st);
+    return e;
 }
 
 template <int DK>
-hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, hipStream_t st) {
+hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, const void *Q, const void *K,
+                       hipStream_t st) {
     switch (chunk) {
-    case 64: return launch_chunk<DK, 64>(c, a, st);
-    case 128: return launch_chunk<DK, 128>(c, a, st);
-    case 256: return launch_chunk<DK, 256>(c, a, st);
+    case 64: return launch_chunk<DK, 64>(c, a, Q, K, st);
+    case 128: return launch_chunk<DK, 128>(c, a, Q, K, st);
+    case 256: return launch_chunk<DK, 256>(c, a, Q, K, st);
     default: return hipErrorNotSupported;
     }
 }
 
 struct MfmaPlan {
-    size_t cs = 0, qr = 0, kr = 0, stats = 0, total = 0;
+    size_t qf = 0, kf = 0, pf = 0, stats = 0, total = 0;
 };
 
-// workspace: [cos/sin table][Q~ bf16][K~ bf16][slice statistics]
-MfmaPlan mfma_plan(const msr_problem *p) {
+// workspace: [QF][KF][PF][slice statistics]
+MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     MfmaPlan m;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t qk = (size_t)p->B * p->T * p->H * p->dk * 2;
-    m.cs = 0;
-    m.qr = up((size_t)p->T * (p->dk / 2) * sizeof(float2));
-    m.kr = m.qr + up(qk);
-    m.stats = m.kr + up(qk);
+    const size_t tokens = (size_t)p->B * p->T * p->H;  // token-heads
+    m.qf = 0;
+    m.kf = m.qf + up(tokens * p->dk * 2);
+    m.pf = m.kf + up(tokens * p->dk * 2);
+    // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
+    m.stats = m.pf + up(tokens * chunk * 2);
     const int NS = p->dv / W;
-    m.total = m.stats + (NS > 1 ? up((size_t)p->B * p->T * p->H * NS * sizeof(float2)) : 0);
+    m.total = m.stats + (NS > 1 ? up(tokens * NS * sizeof(float2)) : 0);
     return m;
 }
 
@@ -649,18 +780,18 @@ bool mfma_supported(const msr_problem *p, int form, int chunk) {
 
 size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk) {
     if (!mfma_supported(p, form, chunk)) return 0;
-    return mfma_plan(p).total;
+    return mfma_plan(p, chunk).total;
 }
 
 hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, const void *Q,
                           const void *K, const void *V, void *O, const float *s_in, float *s_out,
                           void *ws, hipStream_t st) {
-    const MfmaPlan m = mfma_plan(p);
+    const MfmaPlan m = mfma_plan(p, chunk);
     char *wsb = static_cast<char *>(ws);
-    const bool rotate = !(c.flags & MSR_FLAG_NO_ROTATE);
     ChunkArgs a;
-    a.q = rotate ? reinterpret_cast<const uint16_t *>(wsb + m.qr) : static_cast<const uint16_t *>(Q);
-    a.k = rotate ? reinterpret_cast<const uint16_t *>(wsb + m.kr) : static_cast<const uint16_t *>(K);
+    a.qf = reinterpret_cast<const uint16_t *>(wsb + m.qf);
+    a.kf = reinterpret_cast<const uint16_t *>(wsb + m.kf);
+    a.pf = reinterpret_cast<const uint16_t *>(wsb + m.pf);
     a.v = static_cast<const uint16_t *>(V);
     a.o = static_cast<uint16_t *>(O);
     a.s_in = s_in;
@@ -669,34 +800,16 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.stats = a.NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
 
     hipError_t e = hipSuccess;
-    if (rotate) {
-        float2 *cs = reinterpret_cast<float2 *>(wsb + m.cs);
-        const size_t ncs = (size_t)p->T * (p->dk / 2);
-        size_t g = (ncs + 255) / 256;
-        if (g > 65536) g = 65536;
-        hipLaunchKernelGGL(angle_table_kernel, dim3((unsigned)g), dim3(256), 0, st, c, cs);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const size_t n8 = (size_t)p->B * p->T * p->H * (p->dk / 8);
-        g = (n8 + 255) / 256;
-        if (g > 262144) g = 262144;
-        hipLaunchKernelGGL(rotate_qk_kernel, dim3((unsigned)g), dim3(256), 0, st, c, cs,
-                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
-                           reinterpret_cast<uint16_t *>(wsb + m.qr), reinterpret_cast<uint16_t *>(wsb + m.kr));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    main_kernel_begin(st);
     switch (p->dk) {
-    case 64: e = dispatch_bc<64>(c, a, chunk, st); break;
-    case 128: e = dispatch_bc<128>(c, a, chunk, st); break;
-    case 256: e = dispatch_bc<256>(c, a, chunk, st); break;
+    case 64: e = dispatch_bc<64>(c, a, chunk, Q, K, st); break;
+    case 128: e = dispatch_bc<128>(c, a, chunk, Q, K, st); break;
+    case 256: e = dispatch_bc<256>(c, a, chunk, Q, K, st); break;
     default: e = hipErrorNotSupported;
     }
-    main_kernel_end(st);
     if (e != hipSuccess) return e;
     if (a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;
-        const int RB = 256 / (p->dv / 8);
-        const size_t blocks = (rows + RB - 1) / RB;
+        const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
         hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, a.NS,
                            a.stats, a.o, rows);
         e = hipGetLastError();
