@@ -20,7 +20,8 @@
 //   QF[pair][chunk][u][ks]  Q~, query rows 16 u.., d_k columns 32 ks..
 //                           (B operand of the inter-chunk product)
 //   KF[pair][chunk][rt][kb] (K~ zeta s)^T, d_k rows 16 rt.., tokens 32 kb..
-//                           with zeta_t s = s gamma^(b-1-t) applied
+//                           with zeta_t s = s gamma^(b-1-t) and the rescale
+//                           factor gamma^(-b j) of the chunk applied
 //                           (A operand of the state update)
 //   PF[pair][chunk][u][kb]  P^T, keys 32 kb.., query columns 16 u.., keys in
 //                           the order {4g..4g+3, 16+4g..16+4g+3} of lane
@@ -35,8 +36,9 @@
 //   - the chunk's V slice is in LDS (direct global->LDS loads issued one
 //     chunk ahead into the other of two buffers);
 //   - O^T = (S_old^T Q~^T) (.) xi, with S_old^T as bf16 in LDS;
-//   - S = gamma^b S, then per 32-key block S += (K~ zeta s)^T V and
-//     O^T += V^T P^T; V and V^T come from the gfx950 LDS transpose read
+//   - per 32-key block S^ += (K~ zeta s)^T V and O^T += V^T P^T, where S^ is
+//     the state up to a power of gamma that changes only every m chunks
+//     (rescale_period); V and V^T come from the gfx950 LDS transpose read
 //     (ds_read_b64_tr_b16);
 //   - GroupNorm of each output row over the slice (final when W == d_v,
 //     otherwise (mean, M2) partials for gn_finalize_kernel);
@@ -118,11 +120,28 @@ __device__ __forceinline__ void load_lds16(const void *gptr, void *lds) {
 // Keeps the scheduler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Keeps global-memory instructions (loads, stores, direct-to-LDS loads) in
+// program order across this point; ALU, MFMA and LDS instructions may still
+// move across it.
+__device__ __forceinline__ void vmem_fence() { __builtin_amdgcn_sched_barrier(0x078F); }
+
 // s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The chunk kernel carries S^ = S gamma^(-b j) instead of the state S, where
+// j = (chunk index) mod m: within a run of m chunks the update is then a
+// plain accumulation S^ += gamma^(-b j) K~^T (V (.) zeta) (the factor rides
+// on the K~^T fragments), and S^ is multiplied by a power of gamma only when
+// a run starts.  m is the largest period with gamma^(-b (m-1)) <= 2^40, so S^
+// stays far from the fp32 range limits; gamma = 1 never rescales.
+__device__ __forceinline__ int rescale_period(float lg, int bc) {
+    const float per = (float)bc * -lg;  // -log2(gamma^b) >= 0
+    const float m = per > 0.f ? 40.f / per + 1.f : 1e9f;
+    return m >= (float)(1 << 30) ? (1 << 30) : (int)m;
 }
 
 template <int DK, int BC>
@@ -228,7 +247,8 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += NT) {
         dec[t] = c.scale * exp2f((float)t * lg);
-        zet[t] = c.scale * exp2f((float)(BC - 1 - t) * lg);
+        // s gamma^(BC-1-t) gamma^(-BC j), j = chunk index mod the rescale period
+        zet[t] = c.scale * exp2f((float)(BC - 1 - t - BC * (ci % rescale_period(lg, BC))) * lg);
     }
 
     const uint32_t rowQK = (uint32_t)c.H * DK * 2;  // bytes between tokens of Q, K
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     __syncthreads();
 
     // ---- (K~ zeta s)^T fragments: lane (n, g) of fragment (rt, kb) holds
-    // K~[t][16 rt + n] s gamma^(BC-1-t) for t = 32 kb + 8 g + e
+    // K~[t][16 rt + n] s gamma^(BC-1-t) gamma^(-BC j) for t = 32 kb + 8 g + e
     uint16_t *kfo = kf + (size_t)blockIdx.x * (C::RT * C::NB * FRAG) + lane * 8;
     for (int f = w; f < C::RT * C::NB; f += PW) {
         const int rt = f / C::NB, kb = f % C::NB;
@@ -362,7 +382,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     __shared__ __attribute__((aligned(16))) __bf16 St0[W * C::SP], St1[W * C::SP];  // S_old^T
     __shared__ float xi[BC];  // gamma^(j+1)
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform across the wave: keep it (and what derives
+    // from it) in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     // workgroup -> (pair, slice): the slices of one pair get ids equal mod 8,
     // i.e. run on the same XCD and share its L2 for the pair's fragments
@@ -383,13 +405,19 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const int col0 = slice * W;
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += C::THREADS) xi[t] = exp2f((float)(t + 1) * lg);
-    const float gb = exp2f((float)BC * lg);
+    const int period = rescale_period(lg, BC);
+    int ph = 0;  // the carried S^ is S gamma^(-BC ph)
 
     const int nch = c.T / BC;
     const size_t pc0 = (size_t)pair * nch;  // (pair, chunk 0) index of the fragments
-    const uint16_t *qfb = a.qf + pc0 * (C::NKT * C::KS * FRAG) + lane * 8;
-    const uint16_t *kfb = a.kf + pc0 * (C::RT * C::NB * FRAG) + lane * 8;
-    const uint16_t *pfb = a.pf + pc0 * (C::NKT * C::NB * FRAG) + lane * 8;
+    // uniform fragment bases; each lane adds its 16-byte offset
+    const uint16_t *qfb = a.qf + pc0 * (C::NKT * C::KS * FRAG);
+    const uint16_t *kfb = a.kf + pc0 * (C::RT * C::NB * FRAG);
+    const uint16_t *pfb = a.pf + pc0 * (C::NKT * C::NB * FRAG);
+    const uint32_t loff = lane * 16;
+    auto ldfrag = [&](const uint16_t *fb, size_t frag) {
+        return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(fb + frag * FRAG) + loff);
+    };
     const uint32_t rowV = (uint32_t)c.H * c.dv * 2;  // bytes between tokens of V
     const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
 
@@ -421,20 +449,20 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 #pragma unroll
         for (int f = 0; f < C::NQ; ++f)
             if (f >= f0 && f < f1)
-                qr[f / C::KS][f % C::KS] = ldf(qfb + ((size_t)(ci * C::NKT + qt[f / C::KS]) * C::KS + f % C::KS) * FRAG);
+                qr[f / C::KS][f % C::KS] = ldfrag(qfb, (size_t)(ci * C::NKT + qt[f / C::KS]) * C::KS + f % C::KS);
     };
     // K~^T and P^T fragments of block kb of chunk ci into slot kb % R
     auto load_kp_k = [&](int ci, int kb) {
         ci = ci < nch ? ci : nch - 1;
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
-            kr[rt][kb % C::R] = ldf(kfb + ((size_t)(ci * C::RT + rbase + rt) * C::NB + kb) * FRAG);
+            kr[rt][kb % C::R] = ldfrag(kfb, (size_t)(ci * C::RT + rbase + rt) * C::NB + kb);
     };
     auto load_kp_p = [&](int ci, int kb) {
         ci = ci < nch ? ci : nch - 1;
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u)
-            pr[u][kb % C::R] = ldf(pfb + ((size_t)(ci * C::NKT + qt[u]) * C::NB + kb) * FRAG);
+            pr[u][kb % C::R] = ldfrag(pfb, (size_t)(ci * C::NKT + qt[u]) * C::NB + kb);
     };
 
     // ---- state tiles: d_k rows (rbase + rt) 16 + 4 g + r, columns (cbase + ct) 16 + l16
@@ -466,12 +494,15 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     // Before the first chunk they hold zeros for chunk 0's rows, which the
     // real values overwrite later (stores of one wave to one address stay in
     // order), so that every chunk issues the same stores.
+    // row offsets are 32-bit within the batch row: T H d_v < 2^31
+    uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 4 * g;
+    float2 *sbase_st = a.stats ? a.stats + (size_t)b * c.T * c.H * a.NS + slice : nullptr;
     uint32_t pend_o[C::NQT][C::CT][2];
-    size_t pend_row[C::NQT];
+    uint32_t pend_row[C::NQT];  // t H + h within the batch row
     float2 pend_stat[C::NQT];
 #pragma unroll
     for (int u = 0; u < C::NQT; ++u) {
-        pend_row[u] = ((size_t)b * c.T + 16 * qt[u] + l16) * c.H + h;
+        pend_row[u] = (uint32_t)(16 * qt[u] + l16) * c.H + h;
         pend_stat[u] = make_float2(0.f, 0.f);
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
@@ -479,13 +510,13 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     auto flush_u = [&](int u) {
-        uint16_t *dst = a.o + pend_row[u] * c.dv + col0 + 4 * g;
+        uint16_t *dst = obase + pend_row[u] * (uint32_t)c.dv;
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) {
             const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
             *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
         }
-        if (stats_out && g == 0) a.stats[pend_row[u] * a.NS + slice] = pend_stat[u];
+        if (stats_out && g == 0) sbase_st[pend_row[u] * (uint32_t)a.NS] = pend_stat[u];
     };
     auto flush = [&]() {
 #pragma unroll
@@ -526,54 +557,60 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             }
         };
         {
-            bf16x8 fa[C::CT], fb[C::CT];
-#pragma unroll
-            for (int u = 0; u < C::NQT; ++u)
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 fr[2][C::CT];  // S_old^T fragments of k-steps ks (even/odd)
 #pragma unroll
             for (int ct = 0; ct < C::CT; ++ct)
-                fa[ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 8 * g);
+                fr[0][ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 8 * g);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 if (ks + 1 < C::KS) {
 #pragma unroll
                     for (int ct = 0; ct < C::CT; ++ct)
-                        fb[ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
+                        fr[(ks + 1) & 1][ct] =
+                            *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 32 * (ks + 1) + 8 * g);
                 }
-                sched_fence();
+                vmem_fence();
 #pragma unroll
                 for (int u = 0; u < C::NQT; ++u)
 #pragma unroll
-                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = mfma16(fa[ct], qr[u][ks], oacc[u][ct]);
-                sched_fence();
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        oacc[u][ct] = mfma16(fr[ks & 1][ct], qr[u][ks],
+                                             ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[u][ct]);
+                vmem_fence();
                 if (ks < NOPS) op(ks);
-                sched_fence();
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) fa[ct] = fb[ct];
+                vmem_fence();
             }
 #pragma unroll
             for (int i = C::KS; i < NOPS; ++i) op(i);
-            sched_fence();
+            vmem_fence();
+            // S_old = S^ gamma^(BC ph)
+            const float fx = exp2f((float)(BC * ph) * lg);
 #pragma unroll
             for (int u = 0; u < C::NQT; ++u) {
-                const float x = xi[16 * qt[u] + l16];
+                const float x = xi[16 * qt[u] + l16] * fx;
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
             }
         }
+        {  // a new run of the rescale period: S^ = gamma^BC S_old, phase 0
+            const int j = ci % period;
+            if (j == 0) {
+                const float f = exp2f((float)(BC * (1 + ph)) * lg);
 #pragma unroll
-        for (int rt = 0; rt < C::RPW; ++rt)
+                for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * gb;
+                    for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * f;
+            }
+            ph = j;
+        }
 
         // ---- per 32-key block: state update and value product
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
             if (!C::V_FIRST && kb == C::KBV) {
-                sched_fence();
+                vmem_fence();
                 dma_v(ci + 1, Vn);
-                sched_fence();
+                vmem_fence();
             }
             // the block R ahead (in this chunk or the next) reuses this slot
             const int nb = kb + C::R;
@@ -591,9 +628,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 #pragma unroll
                     for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(kr[rt][kb % C::R], bv[ct], S[rt][ct]);
             }
-            sched_fence();
+            vmem_fence();
             load_kp_k(ci2, kb2);
-            sched_fence();
+            vmem_fence();
             {  // O^T += V^T P^T for the query tiles that reach this block
                 s16x4 va[C::CT][2];
 #pragma unroll
@@ -610,17 +647,17 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                         oacc[u][ct] = mfma16(cat(va[ct][0], va[ct][1]), pr[u][kb % C::R], oacc[u][ct]);
                 }
             }
-            sched_fence();
+            vmem_fence();
             load_kp_p(ci2, kb2);
             load_q(ci + 1, C::qpart0(kb), C::qpart0(kb + 1));
-            sched_fence();
+            vmem_fence();
         }
 
         // ---- GroupNorm over each row (lanes l16, l16+16, +32, +48 share a query)
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u) {
             const int jq = 16 * qt[u] + l16;
-            pend_row[u] = ((size_t)b * c.T + t0 + jq) * c.H + h;
+            pend_row[u] = (uint32_t)(t0 + jq) * c.H + h;
             if (norm_here || stats_out) {
                 float sum = 0.f;
 #pragma unroll
@@ -656,6 +693,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     if (nch > 0) flush();
 
     if (a.s_out) {
+        const float f = exp2f((float)(BC * ph) * lg);
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
@@ -663,7 +701,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                    a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r];
+                    a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r] * f;
                 }
     }
     // the clamped loads of the last chunk may still be in flight
