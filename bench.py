@@ -6,10 +6,13 @@ products, decay mask, cross-chunk term, state carry, GroupNorm) over the
 7B-shaped layer: B=2, T=8192, H=16, d_k=256, d_v=512, chunk 128, bf16 in,
 fp32 state.  `value` is that forward's throughput in tokens/s with inputs
 already resident in HBM.  The same JSON line also reports
-  - roofline: the chunk-recurrence kernel alone, timed with HIP events
-    recorded around it on its own stream (library measurement hook), against
-    the bf16 dense MFMA peak, with algorithmic flops
-    F = (b+1)(d_k+d_v) + 4 d_k d_v per token and head;
+  - roofline: the chunk-recurrence kernel alone (the dominant kernel), timed
+    with HIP events recorded around it on its own stream (library measurement
+    hook), against the bf16 dense MFMA peak, with its algorithmic flops
+    4 d_k d_v (inter-chunk term and state update) + (b+1) d_v (causal value
+    product) per token and head; the scores (b+1) d_k run in the prep kernel.
+    step_tflops counts F = (b+1)(d_k+d_v) + 4 d_k d_v per token and head over
+    the whole call;
   - decode: the recurrent decode step at B=64, H=16, d_k=256, d_v=512 after a
     2048-token chunkwise prefill, 1024 steps, against the HBM peak;
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
@@ -69,7 +72,14 @@ class HipEvents:
 
 
 def chunk_flops(T, H, B, dk, dv, b):
+    """Algorithmic flops of the whole chunkwise forward."""
     return B * T * H * ((b + 1) * (dk + dv) + 4 * dk * dv)
+
+
+def chunk_kernel_flops(T, H, B, dk, dv, b):
+    """Algorithmic flops of the chunk-recurrence kernel: inter-chunk term and
+    state update (2 d_k d_v each) plus the causal value product (b+1) d_v."""
+    return B * T * H * (4 * dk * dv + (b + 1) * dv)
 
 
 def chunk_bytes(T, H, B, dk, dv):
@@ -126,10 +136,12 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     ms = total_ms / steps
     kms = float(np.mean(kern_ms))
     flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
+    kflops = chunk_kernel_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     return {
         "workload": w, "chunk": chunk, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
-        "kernel_ms": kms, "flops": flops, "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
-        "kernel_tflops": flops / (kms / 1e3) / 1e12,
+        "kernel_ms": kms, "flops": flops, "kernel_flops": kflops,
+        "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
+        "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
     }
 
 
@@ -260,7 +272,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": r["kernel_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": r["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic, "kernel": "chunk_mfma_kernel",
-                     "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["flops"]},
+                     "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["kernel_flops"]},
+        "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
         "cpu_baseline": cpu,
         "decode": dec,
         "hbm_view": {"bytes_per_step": r["bytes"],

@@ -6,20 +6,22 @@
 // The step is bound by HBM: every call reads and writes the whole fp32
 // state (B*H*dk*dv*8 bytes) and does 4 flops per state element.  One
 // workgroup per (batch, head) pair streams that pair's state once, in place,
-// with 16-byte accesses: thread (rg, cg) owns columns 4cg..4cg+3 and rows
-// rg, rg+R, ... (R = 256 / (dv/4) row groups), so every wave reads whole
-// contiguous rows.  Rows are processed in batches of U so that U loads are in
-// flight per thread before the first dependent store.  q~ and k~ (rotated,
-// K scaled) are built once per workgroup in LDS; the partial q~ S sums of the
-// row groups meet in LDS, then GroupNorm runs over the d_v outputs.
+// with 16-byte non-temporal accesses: thread (rg, cg) owns columns
+// 4cg..4cg+3 and rows rg, rg+R, ... (R = 512 / (dv/4) row groups), so every
+// wave reads whole contiguous rows.  Rows are processed in batches of U = 16
+// so that 16 loads are in flight per thread before the first dependent
+// store; the first batch is issued before the rotation prologue, whose
+// latency it hides.  q~ and k~ (rotated, K scaled) are built once per
+// workgroup in LDS; the partial q~ S sums of the row groups meet in LDS,
+// then GroupNorm runs over the d_v outputs.
 #include "msr_device.hpp"
 
 namespace {
 
 using namespace msr;
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_U = 8;
+constexpr int DEC_THREADS = 512;
+constexpr int DEC_U = 16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename TIn>
@@ -35,6 +37,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(MsrConst c, const T
     __shared__ float4 part[DEC_THREADS];
     __shared__ float red[16];
 
+    const int G = c.dv / 4;        // float4 column groups per row (<= 256)
+    const int R = DEC_THREADS / G; // row groups
+    const int rg = tid / G, cg = tid - rg * G;
+    const bool active = rg < R;
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(state + static_cast<size_t>(pair) * c.dk * c.dv);
+    // first batch of state rows, in flight during the prologue
+    f32x4 s[DEC_U];
+    if (active) {
+#pragma unroll
+        for (int u = 0; u < DEC_U; ++u) {
+            const int i = rg + u * R;
+            if (i < c.dk) s[u] = __builtin_nontemporal_load(&S4[static_cast<size_t>(i) * G + cg]);
+        }
+    }
+
     const size_t qk_base = static_cast<size_t>(pair) * c.dk;
     for (int i = tid; i < c.dk / 2; i += DEC_THREADS) {
         const float q0 = load(q, qk_base + 2 * i), q1 = load(q, qk_base + 2 * i + 1);
@@ -48,22 +65,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(MsrConst c, const T
     }
     __syncthreads();
 
-    const int G = c.dv / 4;        // float4 column groups per row (<= 256)
-    const int R = DEC_THREADS / G; // row groups
-    const int rg = tid / G, cg = tid - rg * G;
-    const bool active = rg < R;
     const float g = c.gamma[h];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (active) {
         const size_t vb = static_cast<size_t>(pair) * c.dv + 4 * cg;
         const float4 vv = make_float4(load(v, vb), load(v, vb + 1), load(v, vb + 2), load(v, vb + 3));
-        f32x4 *S4 = reinterpret_cast<f32x4 *>(state + static_cast<size_t>(pair) * c.dk * c.dv);
         for (int i0 = rg; i0 < c.dk; i0 += R * DEC_U) {
-            f32x4 s[DEC_U];
+            if (i0 != rg) {  // the first batch is already loaded
 #pragma unroll
-            for (int u = 0; u < DEC_U; ++u) {
-                const int i = i0 + u * R;
-                if (i < c.dk) s[u] = __builtin_nontemporal_load(&S4[static_cast<size_t>(i) * G + cg]);
+                for (int u = 0; u < DEC_U; ++u) {
+                    const int i = i0 + u * R;
+                    if (i < c.dk) s[u] = __builtin_nontemporal_load(&S4[static_cast<size_t>(i) * G + cg]);
+                }
             }
 #pragma unroll
             for (int u = 0; u < DEC_U; ++u) {
