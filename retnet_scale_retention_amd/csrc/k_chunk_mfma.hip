@@ -180,6 +180,9 @@ struct Cfg {
     static constexpr bool V_FIRST = after_v(0) <= 63;
     static constexpr int KBV = V_FIRST ? 0 : first_kbv();
     static constexpr int VWAIT = after_v(KBV);
+    // state-only pass: V first, then only the K~^T fragments of every block
+    static constexpr int VWAIT_SO = NB * RPW;
+    static_assert(VWAIT_SO <= 63, "vmcnt range");
     static_assert(NQT >= 1 && RPW >= 1 && NV >= 1 && (NW / CG) * RPW == RT && CG * CPW == CT, "shape");
     static_assert(VWAIT <= 63 && KBV < NB, "vmcnt range");
     static_assert(2 * VTILE + 2 * W * SP * 2 + 2 * BC * 4 <= 163840, "LDS budget (chunk kernel)");
@@ -207,6 +210,8 @@ struct ChunkArgs {
     float *s_out;
     float2 *stats;  // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
     int NS;         // slices per pair (dv / W)
+    int nseg, seglen;  // segments of seglen chunks per pair (nseg * seglen = T / b)
+    float *segE;       // [pair][nseg][dk][dv] end state of each segment from a zero state
 };
 
 // Per (pair, chunk): rotation of the chunk's Q and K rows (theta_shift,
@@ -373,7 +378,14 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     }
 }
 
-template <int DK, int BC>
+// Segments.  When the (pair, slice) workgroups are too few to fill the GPU,
+// each pair's chunks are split into nseg segments of seglen chunks.  The
+// state-only instantiation (SO) runs segments 0 .. nseg-2 from a zero state
+// with only the state update and writes each end state E_g; the full
+// instantiation then starts segment g from
+//   S_in(g) = gamma^(b seglen) S_in(g-1) + E_(g-1),  S_in(0) = s_in
+// (the chunkwise recurrence regrouped by segments) and writes its outputs.
+template <int DK, int BC, bool SO>
 __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
     // separate LDS objects for the two V buffers, so the compiler can tell the
@@ -386,27 +398,35 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     // from it) in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    // workgroup -> (pair, slice): the slices of one pair get ids equal mod 8,
-    // i.e. run on the same XCD and share its L2 for the pair's fragments
+    // workgroup -> (pair, segment, slice): the slices of one (pair, segment)
+    // get ids equal mod 8, i.e. run on the same XCD and share its L2 for the
+    // fragments they all read
     const int npairs = c.B * c.H;
-    int pair, slice;
+    int pair, seg, slice;
     {
-        const int id = blockIdx.x;
-        if (npairs % 8 == 0) {
+        const int id = blockIdx.x, nps = npairs * a.nseg;
+        int ps;
+        if (nps % 8 == 0) {
             const int xcd = id & 7, j = id >> 3;
-            pair = (j / a.NS) * 8 + xcd;
+            ps = (j / a.NS) * 8 + xcd;
             slice = j % a.NS;
         } else {
-            pair = id / a.NS;
+            ps = id / a.NS;
             slice = id % a.NS;
         }
+        pair = ps / a.nseg;
+        seg = ps % a.nseg;
     }
+    if (SO && seg == a.nseg - 1) return;  // the last segment's end state is not needed
+    const int i0 = seg * a.seglen, i1 = i0 + a.seglen;  // this workgroup's chunks
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * W;
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += C::THREADS) xi[t] = exp2f((float)(t + 1) * lg);
     const int period = rescale_period(lg, BC);
-    int ph = 0;  // the carried S^ is S gamma^(-BC ph)
+    // the carried S^ is S gamma^(-BC ph); entering chunk i0 it has the phase
+    // of chunk i0 - 1
+    int ph = i0 == 0 ? 0 : (i0 - 1) % period;
 
     const int nch = c.T / BC;
     const size_t pc0 = (size_t)pair * nch;  // (pair, chunk 0) index of the fragments
@@ -468,15 +488,28 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     // ---- state tiles: d_k rows (rbase + rt) 16 + 4 g + r, columns (cbase + ct) 16 + l16
     f32x4 S[C::RPW][C::CPW];
     const size_t sbase = (size_t)pair * DK * c.dv + col0;
+    // E_g of this pair: segE + ((pair nseg + g) DK + row) dv + col0 + col
+    const size_t ebase = (size_t)pair * a.nseg * DK * c.dv + col0;
+    {
+        const float gseg = exp2f((float)(BC * a.seglen) * lg);  // gamma^(b seglen)
+        const float f0 = exp2f(-(float)(BC * ph) * lg);         // to the carried scale
 #pragma unroll
-    for (int rt = 0; rt < C::RPW; ++rt)
+        for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < C::CPW; ++ct)
+            for (int ct = 0; ct < C::CPW; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                S[rt][ct][r] = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                    float x = 0.f;
+                    if (!SO) {
+                        x = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
+                        for (int gg = 0; gg < seg; ++gg)
+                            x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
+                        x *= f0;
+                    }
+                    S[rt][ct][r] = x;
+                }
+    }
     auto write_st = [&](__bf16 *St) {
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
@@ -502,7 +535,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     float2 pend_stat[C::NQT];
 #pragma unroll
     for (int u = 0; u < C::NQT; ++u) {
-        pend_row[u] = (uint32_t)(16 * qt[u] + l16) * c.H + h;
+        pend_row[u] = (uint32_t)(i0 * BC + 16 * qt[u] + l16) * c.H + h;
         pend_stat[u] = make_float2(0.f, 0.f);
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
@@ -523,14 +556,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         for (int u = 0; u < C::NQT; ++u) flush_u(u);
     };
 
-    write_st(St0);
-    if (nch > 0) {
-        dma_v(0, Vb0);
-        load_q(0, 0, C::NQ);
+    if (!SO) write_st(St0);
+    if (i1 > i0) {
+        dma_v(i0, Vb0);
+        if (!SO) load_q(i0, 0, C::NQ);
 #pragma unroll
         for (int kb = 0; kb < C::R; ++kb) {
-            load_kp_k(0, kb);
-            load_kp_p(0, kb);
+            load_kp_k(i0, kb);
+            if (!SO) load_kp_p(i0, kb);
         }
     }
 
@@ -539,11 +572,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         const int t0 = ci * BC;
         // this chunk's V slice has landed once at most VWAIT newer operations
         // are outstanding (the prologue issued fewer: wait for all)
-        if (ci == 0)
+        if (ci == i0)
             wait_vm<0>();
+        else if (SO)
+            wait_vm<C::VWAIT_SO>();
         else
             wait_vm<C::VWAIT>();
         __syncthreads();
+        if (SO) dma_v(ci + 1, Vn);
 
         // ---- O^T = (S_old^T Q~^T) xi.  After the MFMAs of k-step ks, memory
         // operation ks of [previous outputs of tile 0..NQT-1, next V units]
@@ -556,7 +592,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 dma_v_unit(ci + 1, i - C::NQT, Vn);
             }
         };
-        {
+        if (!SO) {
             bf16x8 fr[2][C::CT];  // S_old^T fragments of k-steps ks (even/odd)
 #pragma unroll
             for (int ct = 0; ct < C::CT; ++ct)
@@ -607,7 +643,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         // ---- per 32-key block: state update and value product
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
-            if (!C::V_FIRST && kb == C::KBV) {
+            if (!SO && !C::V_FIRST && kb == C::KBV) {
                 vmem_fence();
                 dma_v(ci + 1, Vn);
                 vmem_fence();
@@ -631,7 +667,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             vmem_fence();
             load_kp_k(ci2, kb2);
             vmem_fence();
-            {  // O^T += V^T P^T for the query tiles that reach this block
+            if (!SO) {  // O^T += V^T P^T for the query tiles that reach this block
                 s16x4 va[C::CT][2];
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) {
@@ -648,11 +684,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 }
             }
             vmem_fence();
-            load_kp_p(ci2, kb2);
-            load_q(ci + 1, C::qpart0(kb), C::qpart0(kb + 1));
+            if (!SO) {
+                load_kp_p(ci2, kb2);
+                load_q(ci + 1, C::qpart0(kb), C::qpart0(kb + 1));
+            }
             vmem_fence();
         }
 
+        if (SO) return;
         // ---- GroupNorm over each row (lanes l16, l16+16, +32, +48 share a query)
 #pragma unroll
         for (int u = 0; u < C::NQT; ++u) {
@@ -686,13 +725,24 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         }
         write_st(Sn);
     };
-    for (int ci = 0; ci < nch; ci += 2) {
+    for (int ci = i0; ci < i1; ci += 2) {
         chunk(ci, Vb0, Vb1, St0, St1);
-        if (ci + 1 < nch) chunk(ci + 1, Vb1, Vb0, St1, St0);
+        if (ci + 1 < i1) chunk(ci + 1, Vb1, Vb0, St1, St0);
     }
-    if (nch > 0) flush();
+    if (!SO && i1 > i0) flush();
 
-    if (a.s_out) {
+    if (SO) {  // this segment's end state from a zero state
+        const float f = exp2f((float)(BC * ph) * lg);
+#pragma unroll
+        for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                    a.segE[ebase + ((size_t)seg * DK + row) * c.dv + col] = S[rt][ct][r] * f;
+                }
+    } else if (a.s_out && seg == a.nseg - 1) {
         const float f = exp2f((float)(BC * ph) * lg);
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
@@ -765,9 +815,15 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, co
                        const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int grid = npairs * a.nseg * a.NS;
+    if (a.nseg > 1) {  // end states of segments 0 .. nseg-2
+        auto sk = chunk_mfma_kernel<DK, BC, true>;
+        hipLaunchKernelGGL(sk, dim3(grid), dim3(C::THREADS), 0, st, c, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     main_kernel_begin(st);
-    auto ck = chunk_mfma_kernel<DK, BC>;
-    hipLaunchKernelGGL(ck, dim3(npairs * a.NS), dim3(C::THREADS), 0, st, c, a);
+    auto ck = chunk_mfma_kernel<DK, BC, false>;
+    hipLaunchKernelGGL(ck, dim3(grid), dim3(C::THREADS), 0, st, c, a);
     e = hipGetLastError();
     main_kernel_end(st);
     return e;
@@ -785,8 +841,19 @@ hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, const v
 }
 
 struct MfmaPlan {
-    size_t qf = 0, kf = 0, pf = 0, stats = 0, total = 0;
+    size_t qf = 0, kf = 0, pf = 0, stats = 0, segE = 0, total = 0;
+    int nseg = 1;
 };
+
+// Segments per pair: doubled while the workgroups (pairs x value slices x
+// segments) stay within one per CU and every segment keeps >= 2 chunks.
+int choose_nseg(const msr_problem *p, int chunk) {
+    const int nch = p->T / chunk;
+    const long units = (long)p->B * p->H * (p->dv / W);
+    int g = 1;
+    while (units * g * 2 <= 256 && nch % (g * 2) == 0 && nch / (g * 2) >= 2) g *= 2;
+    return g;
+}
 
 // workspace: [QF][KF][PF][slice statistics]
 MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
@@ -799,7 +866,9 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
     m.stats = m.pf + up(tokens * chunk * 2);
     const int NS = p->dv / W;
-    m.total = m.stats + (NS > 1 ? up(tokens * NS * sizeof(float2)) : 0);
+    m.segE = m.stats + (NS > 1 ? up(tokens * NS * sizeof(float2)) : 0);
+    m.nseg = choose_nseg(p, chunk);
+    m.total = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
     return m;
 }
 
@@ -836,6 +905,9 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.s_out = s_out;
     a.NS = p->dv / W;
     a.stats = a.NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
+    a.nseg = m.nseg;
+    a.seglen = p->T / chunk / m.nseg;
+    a.segE = m.nseg > 1 ? reinterpret_cast<float *>(wsb + m.segE) : nullptr;
 
     hipError_t e = hipSuccess;
     switch (p->dk) {
