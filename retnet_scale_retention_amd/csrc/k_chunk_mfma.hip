@@ -212,6 +212,7 @@ struct ChunkArgs {
     int NS;         // slices per pair (dv / W)
     int nseg, seglen;  // segments of seglen chunks per pair (nseg * seglen = T / b)
     float *segE;       // [pair][nseg][dk][dv] end state of each segment from a zero state
+    int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
 };
 
 // Per (pair, chunk): rotation of the chunk's Q and K rows (theta_shift,
@@ -228,12 +229,19 @@ struct ChunkArgs {
 // (cos theta_i, sin theta_i) -- the angle-addition formula, a few ulp of
 // drift over at most 16 rows.  Q~ goes straight to its fragments in global
 // memory, K~ of the chunk to LDS; the score products read Q~ back from the
-// fragments (visible to the workgroup after the barrier).  P^T fragments of key blocks a query tile does not reach are not written
-// (the chunk kernel loads but never uses them).
-template <int DK, int BC>
+// fragments (visible to the workgroup after the barrier).  P^T fragments of
+// key blocks a query tile does not reach are not written (the chunk kernel
+// loads but never uses them).
+//
+// PAR (parallel form, b = 64): no scores; K~ also goes to fragments in the
+// Q~ layout (kq, the A operand of the parallel kernel's score products), and
+// the KF fragments carry s gamma^(T-1-t) for the state sum
+// S_out = gamma^T S_in + sum_t gamma^(T-1-t) k~_t^T v_t.
+template <int DK, int BC, bool PAR>
 __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
                                                    const uint16_t *__restrict__ k, uint16_t *__restrict__ qf,
-                                                   uint16_t *__restrict__ kf, uint16_t *__restrict__ pf) {
+                                                   uint16_t *__restrict__ kf, uint16_t *__restrict__ pf,
+                                                   uint16_t *__restrict__ kq) {
     using C = Cfg<DK, BC>;
     constexpr int NT = 512, PW = NT / 64;  // threads, waves
     constexpr int C8 = DK / 8;             // 16-byte channel groups per row
@@ -252,8 +260,10 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += NT) {
         dec[t] = c.scale * exp2f((float)t * lg);
-        // s gamma^(BC-1-t) gamma^(-BC j), j = chunk index mod the rescale period
-        zet[t] = c.scale * exp2f((float)(BC - 1 - t - BC * (ci % rescale_period(lg, BC))) * lg);
+        if (PAR)  // s gamma^(T-1-t) for absolute token t
+            zet[t] = c.scale * exp2f((float)(c.T - 1 - ci * BC - t) * lg);
+        else  // s gamma^(BC-1-t) gamma^(-BC j), j = chunk index mod the rescale period
+            zet[t] = c.scale * exp2f((float)(BC - 1 - t - BC * (ci % rescale_period(lg, BC))) * lg);
     }
 
     const uint32_t rowQK = (uint32_t)c.H * DK * 2;  // bytes between tokens of Q, K
@@ -294,8 +304,9 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
             }
             // fragment (u, ks) = (row / 16, c8 / 4), lane 16 (c8 % 4) + row % 16
             const int row = r0 + j;
-            *reinterpret_cast<u32x4 *>(qfo + (size_t)((row >> 4) * C::KS + (c8 >> 2)) * FRAG +
-                                       (16 * (c8 & 3) + (row & 15)) * 8) = rot ? yq : xq[j];
+            const size_t fo = (size_t)((row >> 4) * C::KS + (c8 >> 2)) * FRAG + (16 * (c8 & 3) + (row & 15)) * 8;
+            *reinterpret_cast<u32x4 *>(qfo + fo) = rot ? yq : xq[j];
+            if (PAR) *reinterpret_cast<u32x4 *>(kq + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG) + fo) = rot ? yk : xk[j];
             *reinterpret_cast<u32x4 *>(Ks + C::koff(row, c8 * 8)) = rot ? yk : xk[j];
             if (rot && j + 1 < RPT) {
 #pragma unroll
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     // ---- P^T = K~ Q~^T per 32-key block, masked, decayed, scaled; wave w
     // takes query tiles w and NKT - 1 - w (or w alone when NKT <= 8)
     constexpr int NU = C::NKT > PW ? 2 : 1;
-    if (w >= C::NKT) return;
+    if (PAR || w >= C::NKT) return;
     int qt[NU];
     qt[0] = w;
     if (NU == 2) qt[NU - 1] = C::NKT - 1 - w;
@@ -417,13 +428,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         pair = ps / a.nseg;
         seg = ps % a.nseg;
     }
-    if (SO && seg == a.nseg - 1) return;  // the last segment's end state is not needed
+    if (SO && !a.par && seg == a.nseg - 1) return;  // the last segment's end state is not needed
     const int i0 = seg * a.seglen, i1 = i0 + a.seglen;  // this workgroup's chunks
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * W;
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += C::THREADS) xi[t] = exp2f((float)(t + 1) * lg);
-    const int period = rescale_period(lg, BC);
+    // (the parallel form's KF fragments carry the whole decay: no rescaling)
+    const int period = a.par ? (1 << 30) : rescale_period(lg, BC);
     // the carried S^ is S gamma^(-BC ph); entering chunk i0 it has the phase
     // of chunk i0 - 1
     int ph = i0 == 0 ? 0 : (i0 - 1) % period;
@@ -506,6 +518,8 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                         for (int gg = 0; gg < seg; ++gg)
                             x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
                         x *= f0;
+                    } else if (a.par && a.s_in) {  // gamma^T s_in
+                        x = a.s_in[sbase + (size_t)row * c.dv + col] * exp2f((float)c.T * lg);
                     }
                     S[rt][ct][r] = x;
                 }
@@ -628,7 +642,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
             }
         }
-        {  // a new run of the rescale period: S^ = gamma^BC S_old, phase 0
+        if (!a.par) {  // a new run of the rescale period: S^ = gamma^BC S_old, phase 0
             const int j = ci % period;
             if (j == 0) {
                 const float f = exp2f((float)(BC * (1 + ph)) * lg);
@@ -731,7 +745,19 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     }
     if (!SO && i1 > i0) flush();
 
-    if (SO) {  // this segment's end state from a zero state
+    if (SO && a.par) {  // the parallel form's outgoing state
+        if (a.s_out) {
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                        a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r];
+                    }
+        }
+    } else if (SO) {  // this segment's end state from a zero state
         const float f = exp2f((float)(BC * ph) * lg);
 #pragma unroll
         for (int rt = 0; rt < C::RPW; ++rt)
@@ -756,6 +782,156 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     }
     // the clamped loads of the last chunk may still be in flight
     __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Parallel form (jsqmd.com s4.1; aiqz.cc "parallel representation"):
+//   O[n] = GN( sum_{m<=n} s gamma^(n-m) (q~_n . k~_m) v_m + gamma^(n+1) q~_n S_in )
+// One workgroup of four waves per (pair, block of 64 queries, 64-column
+// value slice); wave w owns query tile 4 qb + w.  Per 32-key block up to the
+// diagonal, the K~ fragments (prep_kernel, PAR) and the V slice stream into
+// double-buffered LDS by direct loads; each wave forms P^T = K~ Q~^T with
+// bf16 MFMA, applies s gamma^(n-m) and the causal mask in registers, and
+// feeds P^T (two result tiles, keys in the order {4g..4g+3, 16+4g..}) as the
+// B operand of O^T += V^T P^T, V^T read in that order with the transpose
+// read.  The incoming-state term comes first, with S_in^T staged in LDS as
+// bf16.  GroupNorm as in the chunk kernel.
+struct ParArgs {
+    const uint16_t *qf, *kq;  // Q~ and K~ fragments (prep_kernel<dk, 64, PAR>)
+    const uint16_t *v;
+    uint16_t *o;
+    const float *s_in;
+    float2 *stats;
+    int NS;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs a) {
+    using C = Cfg<DK, 64>;
+    constexpr int KS = DK / 32;
+    constexpr int KBYTES = 2 * KS * 1024;  // K~ fragments of one 32-key block
+    constexpr int VBYTES = 32 * W * 2;     // V slice of one 32-key block
+    __shared__ __attribute__((aligned(16))) char Kb0[KBYTES], Kb1[KBYTES];
+    __shared__ __attribute__((aligned(16))) char Vb0[VBYTES], Vb1[VBYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_in^T slice
+
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int nqb = c.T / 64;
+    const int slice = blockIdx.x % a.NS, qb = (blockIdx.x / a.NS) % nqb, pair = blockIdx.x / a.NS / nqb;
+    const int b = pair / c.H, h = pair % c.H;
+    const int col0 = slice * W;
+    const float lg = c.log2g[h];
+    const int tile = 4 * qb + w;              // this wave's query tile
+    const int n = 16 * tile + l16;            // this lane's query row (as MFMA column)
+    const uint32_t loff = lane * 16;
+    const uint16_t *qfb = a.qf + (size_t)pair * nqb * (4 * KS * FRAG);
+    const uint16_t *kqb = a.kq + (size_t)pair * nqb * (4 * KS * FRAG);
+    const uint32_t rowV = (uint32_t)c.H * c.dv * 2;
+    const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
+
+    // key block kb: K~ fragments of key tiles 2 kb, 2 kb + 1 are 2 KS
+    // consecutive fragments of the Q~-layout array; V rows 32 kb ..
+    auto dma = [&](int kb, char *kd, char *vd) {
+        const char *ks = reinterpret_cast<const char *>(kqb + (size_t)(2 * kb) * KS * FRAG);
+        for (int u = w; u < 2 * KS; u += 4) load_lds16(ks + u * 1024 + loff, kd + u * 1024);
+        const int byte = w * 1024 + lane * 16;
+        const int row = byte / (W * 2), phys = (byte % (W * 2)) >> 4;
+        load_lds16(vb + (uint32_t)(32 * kb + row) * rowV + (phys ^ C::swz_v(row)) * 16, vd + w * 1024);
+    };
+
+    bf16x8 qr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qr[ks] = *reinterpret_cast<const bf16x8 *>(
+            reinterpret_cast<const char *>(qfb + (size_t)(tile * KS + ks) * FRAG) + loff);
+
+    f32x4 oacc[C::CT];
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.s_in) {  // (S_in^T Q~^T) gamma^(n+1)
+        const float *sp = a.s_in + (size_t)pair * DK * c.dv + col0;
+        for (int e = tid; e < DK * W; e += 256) {
+            const int row = e / W, col = e % W;
+            St[col * C::SP + row] = static_cast<__bf16>(sp[(size_t)row * c.dv + col]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct)
+                oacc[ct] = mfma16(*reinterpret_cast<const bf16x8 *>(St + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g),
+                                  qr[ks], oacc[ct]);
+        const float x = exp2f((float)(n + 1) * lg);
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * x;
+    }
+
+    const int nkb = 2 * qb + 2;  // key blocks up to the block's last query
+    dma(0, Kb0, Vb0);
+    auto block = [&](int kb, const char *Kc, const char *Vc, char *Kn, char *Vn) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kb + 1 < nkb) dma(kb + 1, Kn, Vn);
+        if (32 * kb > n - l16 + 15) return;  // the whole tile is before this block
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int v2 = 0; v2 < 2; ++v2)
+                acc[v2] = mfma16(*reinterpret_cast<const bf16x8 *>(Kc + (v2 * KS + ks) * 1024 + loff), qr[ks], acc[v2]);
+        bf16x8 pb;
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 32 * kb + 16 * v2 + 4 * g + r;
+                pb[4 * v2 + r] =
+                    static_cast<__bf16>(m <= n ? acc[v2][r] * c.scale * exp2f((float)(n - m) * lg) : 0.f);
+            }
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) {
+            const int col = ct * 16 + 4 * (l16 & 3);
+            const s16x4 v0 = lds_tr(Vc + C::voff(4 * g + (l16 >> 2), col));
+            const s16x4 v1 = lds_tr(Vc + C::voff(16 + 4 * g + (l16 >> 2), col));
+            oacc[ct] = mfma16(cat(v0, v1), pb, oacc[ct]);
+        }
+    };
+    for (int kb = 0; kb < nkb; kb += 2) {
+        block(kb, Kb0, Vb0, Kb1, Vb1);
+        if (kb + 1 < nkb) block(kb + 1, Kb1, Vb1, Kb0, Vb0);
+    }
+
+    // GroupNorm (in-wave when d_v == 64, else slice statistics) and store
+    const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    const uint32_t rowi = (uint32_t)n * c.H + h;  // token-head row within the batch row
+    if (norm_here || stats_out) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) sum += oacc[ct][0] + oacc[ct][1] + oacc[ct][2] + oacc[ct][3];
+        const float mean = sum_lane_groups(sum) * (1.f / W);
+        float m2 = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m2 += (oacc[ct][r] - mean) * (oacc[ct][r] - mean);
+        m2 = sum_lane_groups(m2);
+        if (stats_out && g == 0)
+            a.stats[((size_t)b * c.T * c.H + rowi) * a.NS + slice] = make_float2(mean, m2);
+        if (norm_here) {
+            const float inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[ct][r] = (oacc[ct][r] - mean) * inv;
+        }
+    }
+    uint16_t *dst = a.o + ((size_t)b * c.T * c.H + rowi) * c.dv + col0 + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+        const u32x2 v2 = {pack_bf16x2(oacc[ct][0], oacc[ct][1]), pack_bf16x2(oacc[ct][2], oacc[ct][3])};
+        *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+    }
 }
 
 // GroupNorm of rows whose slices wrote (mean, M2) statistics over W values
@@ -808,11 +984,11 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, co
 template <int DK, int BC>
 hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, hipStream_t st) {
     const int npairs = c.B * c.H;
-    auto pk = prep_kernel<DK, BC>;
+    auto pk = prep_kernel<DK, BC, false>;
     using C = Cfg<DK, BC>;
     hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(512), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
-                       const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf));
+                       const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = npairs * a.nseg * a.NS;
@@ -872,14 +1048,88 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     return m;
 }
 
+// parallel form workspace: [QF][KQ][KF][slice statistics], blocks of 64
+struct ParPlan {
+    size_t qf = 0, kq = 0, kf = 0, stats = 0, total = 0;
+};
+ParPlan par_plan(const msr_problem *p) {
+    ParPlan m;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t tokens = (size_t)p->B * p->T * p->H;
+    const size_t frag = up(tokens * p->dk * 2);
+    m.kq = frag;
+    m.kf = 2 * frag;
+    m.stats = 3 * frag;
+    const int NS = p->dv / W;
+    m.total = m.stats + (NS > 1 ? up(tokens * NS * sizeof(float2)) : 0);
+    return m;
+}
+
+template <int DK>
+hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *Q, const void *K, const void *V,
+                           void *O, const float *s_in, float *s_out, void *ws, hipStream_t st) {
+    const ParPlan m = par_plan(p);
+    char *wsb = static_cast<char *>(ws);
+    const int npairs = c.B * c.H, nqb = c.T / 64, NS = c.dv / W;
+    uint16_t *qf = reinterpret_cast<uint16_t *>(wsb + m.qf), *kq = reinterpret_cast<uint16_t *>(wsb + m.kq);
+    uint16_t *kf = reinterpret_cast<uint16_t *>(wsb + m.kf);
+    float2 *stats = NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
+    auto pk = prep_kernel<DK, 64, true>;
+    hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(512), 0, st, c, static_cast<const uint16_t *>(Q),
+                       static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NS};
+    main_kernel_begin(st);
+    auto ok = parallel_mfma_kernel<DK>;
+    hipLaunchKernelGGL(ok, dim3(npairs * nqb * NS), dim3(256), 0, st, c, pa);
+    e = hipGetLastError();
+    main_kernel_end(st);
+    if (e != hipSuccess) return e;
+    // outgoing state after the outputs, which read s_in (s_out may alias it)
+    if (s_out) {
+        ChunkArgs a{};
+        a.qf = qf;
+        a.kf = kf;
+        a.pf = nullptr;
+        a.v = static_cast<const uint16_t *>(V);
+        a.o = static_cast<uint16_t *>(O);
+        a.s_in = s_in;
+        a.s_out = s_out;
+        a.stats = nullptr;
+        a.NS = NS;
+        a.nseg = 1;
+        a.seglen = nqb;
+        a.segE = nullptr;
+        a.par = 1;
+        auto sk = chunk_mfma_kernel<DK, 64, true>;
+        hipLaunchKernelGGL(sk, dim3(npairs * NS), dim3(Cfg<DK, 64>::THREADS), 0, st, c, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+        const size_t rows = (size_t)p->B * p->T * p->H;
+        const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
+        hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, NS, stats,
+                           static_cast<uint16_t *>(O), rows);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
 }  // namespace
 
 bool mfma_supported(const msr_problem *p, int form, int chunk) {
-    if (form != MSR_FORM_CHUNKWISE || p->dtype != MSR_BF16) return false;
+    if (p->dtype != MSR_BF16) return false;
     if (p->dk != 64 && p->dk != 128 && p->dk != 256) return false;
     if (p->dv % W != 0) return false;
-    if (chunk != 64 && chunk != 128 && chunk != 256) return false;
-    if (chunk > p->T || p->T % chunk != 0) return false;
+    if (form == MSR_FORM_PARALLEL) {
+        if (p->T < 64 || p->T % 64 != 0) return false;
+    } else if (form == MSR_FORM_CHUNKWISE) {
+        if (chunk != 64 && chunk != 128 && chunk != 256) return false;
+        if (chunk > p->T || p->T % chunk != 0) return false;
+    } else {
+        return false;
+    }
     // per-thread byte offsets within one batch row are 32-bit
     if ((uint64_t)p->T * p->H * (p->dk > p->dv ? p->dk : p->dv) * 2 >= (1ull << 32)) return false;
     return true;
@@ -887,7 +1137,7 @@ bool mfma_supported(const msr_problem *p, int form, int chunk) {
 
 size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk) {
     if (!mfma_supported(p, form, chunk)) return 0;
-    return mfma_plan(p, chunk).total;
+    return form == MSR_FORM_PARALLEL ? par_plan(p).total : mfma_plan(p, chunk).total;
 }
 
 hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, const void *Q,
@@ -927,7 +1177,12 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     return e;
 }
 
-hipError_t mfma_parallel(const MsrConst &, const msr_problem *, const void *, const void *,
-                         const void *, void *, const float *, float *, void *, hipStream_t) {
-    return hipErrorNotSupported;
+hipError_t mfma_parallel(const MsrConst &c, const msr_problem *p, const void *Q, const void *K, const void *V,
+                         void *O, const float *s_in, float *s_out, void *ws, hipStream_t st) {
+    switch (p->dk) {
+    case 64: return launch_parallel<64>(c, p, Q, K, V, O, s_in, s_out, ws, st);
+    case 128: return launch_parallel<128>(c, p, Q, K, V, O, s_in, s_out, ws, st);
+    case 256: return launch_parallel<256>(c, p, Q, K, V, O, s_in, s_out, ws, st);
+    default: return hipErrorNotSupported;
+    }
 }

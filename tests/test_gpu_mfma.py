@@ -131,3 +131,70 @@ def test_mfma_segments_vs_oracle(case):
         eo, es = out_err(o, ro), state_err(st, rs)
         note(f"  O err {eo:.2e}  state err {es:.2e}")
         assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+# The bf16 parallel form (T a multiple of 64) runs its own MFMA kernel: causal
+# score blocks per 64-query block with the decay applied in registers, the
+# incoming-state term from S_in^T, and the outgoing state as one decayed sum.
+PAR_CASES = [  # (B, T, H, dk, dv)
+    (1, 64, 2, 64, 64),
+    (2, 192, 2, 64, 128),
+    (1, 512, 2, 128, 64),
+    (1, 320, 2, 128, 192),
+    (1, 256, 2, 256, 64),
+    (1, 512, 1, 256, 128),
+]
+
+
+def run_parallel(q, k, v, g, s_in=None, **kw):
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    qd, kd, vd = (up(x, "bf16", dev) for x in (q, k, v))
+    sd = None if s_in is None else torch.from_numpy(s_in).to(dev)
+    o, s = msr.msr_parallel(qd, kd, vd, g, state_in=sd, **kw)
+    torch.cuda.synchronize()
+    return down(o), down(s)
+
+
+@pytest.mark.parametrize("case", PAR_CASES, ids=lambda c: "B%dT%dH%ddk%ddv%d" % c)
+def test_mfma_parallel_vs_oracle(case):
+    B, T, H, dk, dv = case
+    w = mi.Workload("mfma-par", 36, B, T, H, dk, dv, "bf16", (T,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = mi.gammas(H)
+    note(f"parallel {case}: oracle")
+    ro, rs = orc.parallel(q, k, v, g, s_in=s, pos0=7)
+    o, st = run_parallel(q, k, v, g, s_in=s, pos0=7)
+    eo, es = out_err(o, ro), state_err(st, rs)
+    note(f"  O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+    # the GPU's parallel and chunkwise forms agree
+    oc, sc = run(q, k, v, g, 64, s_in=s, pos0=7)
+    assert out_err(o, oc) < TOL["bf16"] and state_err(st, sc) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_mfma_parallel_flags(flags):
+    w = mi.Workload("mfma-par-flags", 37, 1, 256, 2, 128, 128, "bf16", (256,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(2)
+    ro, rs = orc.parallel(q, k, v, g, rotate=not (flags & 1), groupnorm=not (flags & 2))
+    o, st = run_parallel(q, k, v, g, flags=flags)
+    assert out_err(o, ro) < TOL["bf16"] and state_err(st, rs) < TOL["bf16"]
+
+
+def test_mfma_parallel_state_out_aliases_state_in():
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    w = mi.Workload("mfma-par-alias", 38, 1, 192, 2, 64, 128, "bf16", (192,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = mi.gammas(2)
+    ro, rs = orc.parallel(q, k, v, g, s_in=s)
+    qd, kd, vd = (up(x, "bf16", dev) for x in (q, k, v))
+    sd = torch.from_numpy(s).to(dev)
+    o, s2 = msr.msr_parallel(qd, kd, vd, g, state_in=sd, state_out=sd)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == sd.data_ptr()
+    assert out_err(down(o), ro) < TOL["bf16"] and state_err(down(sd), rs) < TOL["bf16"]
