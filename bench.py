@@ -15,10 +15,13 @@ already resident in HBM.  The same JSON line also reports
     the whole call;
   - decode: the recurrent decode step at B=64, H=16, d_k=256, d_v=512 after a
     2048-token chunkwise prefill, 1024 steps, against the HBM peak;
+  - parallel: the parallel form over the same 7B-shaped layer (O(T^2) score
+    blocks, one call), algorithmic flops (T+1)(d_k+d_v) + 4 d_k d_v per token
+    and head;
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--copy-mib N]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -145,6 +148,44 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     }
 
 
+def bench_parallel(torch, msr, mi, steps):
+    """The parallel form over the 7B-shaped layer (same inputs as the chunkwise leg)."""
+    w = mi.WORKLOADS["7b"]
+    dev = torch.device("cuda:0")
+    q, k, v = mi.qkv(w)
+    up = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    g = mi.gammas(w.H)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g,
+                                        msr.MSR_FORM_PARALLEL, 0), dtype=torch.uint8, device=dev)
+    msr.msr_parallel(qd, kd, vd, g, out=o, state_out=s, workspace=ws)
+    ev = HipEvents(steps)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        msr.set_kernel_events(*ev.pairs[i])
+        msr.msr_parallel(qd, kd, vd, g, out=o, state_out=s, workspace=ws)
+    msr.set_kernel_events(None, None)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    th = w.B * w.T * w.H
+    flops = th * ((w.T + 1) * (w.dk + w.dv) + 4 * w.dk * w.dv)
+    kflops = th * ((w.T + 1) * (w.dk + w.dv) + 2 * w.dk * w.dv)  # output kernel: scores, values, S_in term
+    return {"config": {"B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv}, "ms_per_call": ms,
+            "tokens_per_s": w.B * w.T / (ms / 1e3), "tflops": flops / (ms / 1e3) / 1e12,
+            "kernel": "parallel_mfma_kernel", "kernel_us": kms * 1e3,
+            "kernel_tflops": kflops / (kms / 1e3) / 1e12,
+            "kernel_mfma_frac": kflops / (kms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+
 def bench_decode(torch, msr, mi, nsteps):
     w = mi.WORKLOADS["decode"]
     dev = torch.device("cuda:0")
@@ -224,6 +265,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -245,6 +287,7 @@ def main():
     r = bench_chunkwise(torch, msr, mi, args.steps, args.warmup, args.chunk)
     w = r["workload"]
     dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
+    par = None if args.no_parallel else bench_parallel(torch, msr, mi, 3)
     cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
@@ -276,6 +319,7 @@ def main():
         "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
         "cpu_baseline": cpu,
         "decode": dec,
+        "parallel": par,
         "hbm_view": {"bytes_per_step": r["bytes"],
                      "achieved_GBs": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9,
                      "frac": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS},
