@@ -1145,7 +1145,7 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
                           void *ws, hipStream_t st) {
     const MfmaPlan m = mfma_plan(p, chunk);
     char *wsb = static_cast<char *>(ws);
-    ChunkArgs a;
+    ChunkArgs a{};  // every field starts at zero (par = 0: chunkwise form)
     a.qf = reinterpret_cast<const uint16_t *>(wsb + m.qf);
     a.kf = reinterpret_cast<const uint16_t *>(wsb + m.kf);
     a.pf = reinterpret_cast<const uint16_t *>(wsb + m.pf);

@@ -66,7 +66,7 @@ msr_status check_problem(const msr_problem *p, bool T1) {
 }
 
 MsrConst make_const(const msr_problem *p, int chunk) {
-    MsrConst c;
+    MsrConst c{};
     std::memset(&c, 0, sizeof(c));
     c.B = p->B;
     c.T = p->T;
