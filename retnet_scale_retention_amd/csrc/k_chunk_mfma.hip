@@ -160,6 +160,12 @@ struct Cfg {
     static constexpr int CG = CT / CPW;              // column groups of waves
     static constexpr int R = NB <= 4 ? NB : 1; // key blocks of K~^T / P^T fragments held in registers
     static constexpr int KROW = DK * 2;        // bytes per K~ row in LDS (prep_kernel)
+    // prep_kernel stages Q~ in LDS next to K~ when both fit (1024 threads
+    // when they need more than half of the LDS, so that a CU still holds 16
+    // waves); otherwise Q~ goes straight to its fragments and the scores read
+    // it back from there
+    static constexpr bool QSTAGE = 2 * BC * KROW + 2 * BC * 4 <= 163840;
+    static constexpr int PREP_NT = QSTAGE && 2 * BC * KROW > 81920 ? 1024 : 512;
     static constexpr int VROW = W * 2;         // bytes per V row in LDS
     static constexpr int VTILE = BC * VROW;    // bytes of a chunk's V slice
     static constexpr int NV = VTILE / 1024 / NW;  // direct-load units per wave per chunk
@@ -238,19 +244,21 @@ struct ChunkArgs {
 // the KF fragments carry s gamma^(T-1-t) for the state sum
 // S_out = gamma^T S_in + sum_t gamma^(T-1-t) k~_t^T v_t.
 template <int DK, int BC, bool PAR>
-__global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
-                                                   const uint16_t *__restrict__ k, uint16_t *__restrict__ qf,
-                                                   uint16_t *__restrict__ kf, uint16_t *__restrict__ pf,
-                                                   uint16_t *__restrict__ kq) {
+__global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
+                                                                  const uint16_t *__restrict__ k,
+                                                                  uint16_t *__restrict__ qf, uint16_t *__restrict__ kf,
+                                                                  uint16_t *__restrict__ pf, uint16_t *__restrict__ kq) {
     using C = Cfg<DK, BC>;
-    constexpr int NT = 512, PW = NT / 64;  // threads, waves
-    constexpr int C8 = DK / 8;             // 16-byte channel groups per row
-    constexpr int RG = NT / C8;            // row runs
-    constexpr int RPT = BC / RG;           // rows per run
+    constexpr int NT = C::PREP_NT, PW = NT / 64;  // threads, waves
+    constexpr int C8 = DK / 8;                    // 16-byte channel groups per row
+    constexpr int RG = NT / C8;                   // row runs
+    constexpr int RPT = BC / RG;                  // rows per run
+    constexpr bool QS = C::QSTAGE;
     static_assert(RPT >= 1 && RG * RPT == BC, "row runs");
-    static_assert(BC * C::KROW + BC * 4 <= 163840, "LDS budget (prep kernel)");
-    __shared__ __attribute__((aligned(16))) char Ks[BC * C::KROW];  // K~, swizzled rows
-    __shared__ float dec[BC], zet[BC];                                // s gamma^d, s gamma^(BC-1-t)
+    static_assert((QS ? 2 : 1) * BC * C::KROW + 2 * BC * 4 <= 163840, "LDS budget (prep kernel)");
+    __shared__ __attribute__((aligned(16))) char Ks[BC * C::KROW];            // K~, swizzled rows
+    __shared__ __attribute__((aligned(16))) char Qs[QS ? BC * C::KROW : 16];  // Q~, the same layout
+    __shared__ float dec[BC], zet[BC];  // s gamma^d, s gamma^(BC-1-t)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
     const char *krow = reinterpret_cast<const char *>(k + base);
 
     uint16_t *qfo = qf + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG);
-    {  // ---- rotation: Q~ to its fragments, K~ into LDS
+    {  // ---- rotation: Q~ into LDS (or to its fragments), K~ into LDS
         const int c8 = tid % C8, r0 = (tid / C8) * RPT;
         u32x4 xq[RPT], xk[RPT];
 #pragma unroll
@@ -305,7 +313,10 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
             // fragment (u, ks) = (row / 16, c8 / 4), lane 16 (c8 % 4) + row % 16
             const int row = r0 + j;
             const size_t fo = (size_t)((row >> 4) * C::KS + (c8 >> 2)) * FRAG + (16 * (c8 & 3) + (row & 15)) * 8;
-            *reinterpret_cast<u32x4 *>(qfo + fo) = rot ? yq : xq[j];
+            if (QS)
+                *reinterpret_cast<u32x4 *>(Qs + C::koff(row, c8 * 8)) = rot ? yq : xq[j];
+            else
+                *reinterpret_cast<u32x4 *>(qfo + fo) = rot ? yq : xq[j];
             if (PAR) *reinterpret_cast<u32x4 *>(kq + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG) + fo) = rot ? yk : xk[j];
             *reinterpret_cast<u32x4 *>(Ks + C::koff(row, c8 * 8)) = rot ? yk : xk[j];
             if (rot && j + 1 < RPT) {
@@ -319,6 +330,27 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
         }
     }
     __syncthreads();
+
+    // ---- Q~ fragments from LDS, one whole fragment per store.  For the
+    // chunkwise form they carry the row factor of the inter-chunk term,
+    //   xi_j gamma^(BC ph) = gamma^(j + 1 + BC ph),  ph = (ci - 1) mod m (0 for ci = 0),
+    // the phase m of the state the chunk kernel carries on entering chunk ci
+    // (rescale_period), so that its product with that state is the term itself.
+    if (QS) {
+        const int ph = ci == 0 ? 0 : (ci - 1) % rescale_period(lg, BC);
+        for (int f = w; f < C::NKT * C::KS; f += PW) {
+            const int u = f / C::KS, ks = f % C::KS, row = 16 * u + l16;
+            const u32x4 x = ld16(Qs, C::koff(row, 32 * ks + 8 * g));
+            u32x4 y = x;
+            if (!PAR) {
+                const float fq = exp2f((float)(row + 1 + BC * ph) * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[i] = pack_bf16x2(__uint_as_float(x[i] << 16) * fq, __uint_as_float(x[i] & 0xffff0000u) * fq);
+            }
+            *reinterpret_cast<u32x4 *>(qfo + (size_t)f * FRAG + lane * 8) = y;
+        }
+    }
 
     // ---- (K~ zeta s)^T fragments: lane (n, g) of fragment (rt, kb) holds
     // K~[t][16 rt + n] s gamma^(BC-1-t) gamma^(-BC j) for t = 32 kb + 8 g + e
@@ -364,7 +396,9 @@ __global__ __launch_bounds__(512) void prep_kernel(MsrConst c, const uint16_t *_
             for (int v2 = 0; v2 < 2; ++v2)
                 ka[v2] = *reinterpret_cast<const bf16x8 *>(Ks + C::koff(32 * kb + 16 * v2 + l16, 32 * ks + 8 * g));
 #pragma unroll
-            for (int u = 0; u < NU; ++u) qb[u] = ldf(qfo + (size_t)(qt[u] * C::KS + ks) * FRAG + lane * 8);
+            for (int u = 0; u < NU; ++u)
+                qb[u] = QS ? __builtin_bit_cast(bf16x8, ld16(Qs, C::koff(16 * qt[u] + l16, 32 * ks + 8 * g)))
+                           : ldf(qfo + (size_t)(qt[u] * C::KS + ks) * FRAG + lane * 8);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
                 if (nd[u]) {
@@ -633,13 +667,16 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 #pragma unroll
             for (int i = C::KS; i < NOPS; ++i) op(i);
             vmem_fence();
-            // S_old = S^ gamma^(BC ph)
-            const float fx = exp2f((float)(BC * ph) * lg);
+            // S_old = S^ gamma^(BC ph), times xi per query row (already in the
+            // Q~ fragments when prep_kernel staged Q~ in LDS)
+            if constexpr (!C::QSTAGE) {
+                const float fx = exp2f((float)(BC * ph) * lg);
 #pragma unroll
-            for (int u = 0; u < C::NQT; ++u) {
-                const float x = xi[16 * qt[u] + l16] * fx;
+                for (int u = 0; u < C::NQT; ++u) {
+                    const float x = xi[16 * qt[u] + l16] * fx;
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
+                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * x;
+                }
             }
         }
         if (!a.par) {  // a new run of the rescale period: S^ = gamma^BC S_old, phase 0
@@ -986,7 +1023,7 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, co
     const int npairs = c.B * c.H;
     auto pk = prep_kernel<DK, BC, false>;
     using C = Cfg<DK, BC>;
-    hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(512), 0, st, c, static_cast<const uint16_t *>(Q),
+    hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                        const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr);
     hipError_t e = hipGetLastError();
@@ -1075,7 +1112,7 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     uint16_t *kf = reinterpret_cast<uint16_t *>(wsb + m.kf);
     float2 *stats = NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
     auto pk = prep_kernel<DK, 64, true>;
-    hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(512), 0, st, c, static_cast<const uint16_t *>(Q),
+    hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
