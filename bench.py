@@ -90,9 +90,12 @@ def chunk_bytes(T, H, B, dk, dv):
 
 
 def kernel_source_sha():
+    """Hash of the kernel sources and the build script (its flags shape the
+    generated code)."""
     h = hashlib.sha256()
     for f in sorted((ROOT / "retnet_scale_retention_amd" / "csrc").glob("*")):
         h.update(f.read_bytes())
+    h.update((ROOT / "retnet_scale_retention_amd" / "build.py").read_bytes())
     return h.hexdigest()[:16]
 
 

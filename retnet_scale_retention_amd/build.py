@@ -21,6 +21,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # packed-fp32 instructions are disabled for all device code
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators in architectural VGPRs where they fit: with accumulators
+# in AGPRs the register allocator chains copies between them around loops,
+# which serialises the matrix pipe (a 16x16x32 bf16 MFMA loop with one wave
+# per SIMD then issues every ~31 clocks instead of ~19)
+MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+MFMA_SOURCES = {"k_chunk_mfma.hip"}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{ROOT / 'include'}", f"-I{CSRC}"]
 
@@ -31,7 +37,8 @@ def sources():
 
 def _compile(src: Path) -> Path:
     obj = BUILD / (src.name + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", str(src), "-o", str(obj)]
+    extra = MFMA_FLAGS if src.name in MFMA_SOURCES else []
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", str(src), "-o", str(obj)]
     if src.suffix == ".cpp":
         cmd = [HIPCC, *COMMON, "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
