@@ -227,6 +227,36 @@ def bench_decode(torch, msr, mi, nsteps):
     step_ms = total_ms / nsteps
     kms = float(np.mean(kern))
     bytes_step = 2 * w.B * w.H * w.dk * w.dv * 4 + w.B * w.H * (2 * w.dk + 2 * w.dv) * 2
+
+    # batched serving: every sequence at its own position (one per batch row)
+    nr = max(8, nsteps // 8)
+    base = torch.tensor([(b * 37) % 4096 for b in range(w.B)], dtype=torch.int64, device=dev)
+    pos = [base + w.T + i for i in range(nr)]
+    evr = HipEvents(nr)
+    torch.cuda.synchronize()
+    for i in range(nr):
+        msr.set_kernel_events(*evr.pairs[i])
+        msr.msr_recurrent_step(qs[i], ks[i], vs[i], state, g, pos[i], out=o)
+    msr.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    rk = float(np.mean([evr.elapsed_ms(i) for i in range(nr)]))
+    evr.close()
+    # multi-token steps: 4 new tokens per sequence per call (chunkwise, chunk 4, state carried)
+    tq = mi.device_normal((w.B, 4, w.H, w.dk), 3007, dev, torch.bfloat16)
+    tk = mi.device_normal((w.B, 4, w.H, w.dk), 3008, dev, torch.bfloat16)
+    tv = mi.device_normal((w.B, 4, w.H, w.dv), 3009, dev, torch.bfloat16)
+    ws = torch.empty(msr.workspace_size(w.B, 4, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, 4),
+                     dtype=torch.uint8, device=dev)
+    mo = torch.empty((w.B, 4, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    msr.msr_chunkwise(tq, tk, tv, g, 4, state_in=state, state_out=state, out=mo, workspace=ws, pos_rows=pos[0])
+    nm = 8
+    torch.cuda.synchronize()
+    tm0 = time.perf_counter()
+    for i in range(nm):
+        msr.msr_chunkwise(tq, tk, tv, g, 4, state_in=state, state_out=state, out=mo, workspace=ws,
+                          pos_rows=pos[0] + 4 * i)
+    torch.cuda.synchronize()
+    mms = (time.perf_counter() - tm0) * 1e3 / nm
     return {
         "config": {"B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "prefill_tokens": w.T, "steps": nsteps},
         "steps_per_s": 1e3 / step_ms, "tokens_per_s": w.B * 1e3 / step_ms,
@@ -235,6 +265,11 @@ def bench_decode(torch, msr, mi, nsteps):
                 "frac": bytes_step / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": bytes_step,
                 "traffic": traffic_record("decode_kernel")},
         "prefill_ms": prefill_ms,
+        "ragged": {"note": "one position per batch row", "steps": nr, "kernel_us": rk * 1e3,
+                   "steps_per_s": 1e3 / rk, "hbm_frac": bytes_step / (rk / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "multi_token": {"note": "4 tokens per sequence per call, chunkwise b=4 on the general-purpose path, "
+                                "rows at their own positions", "calls": nm, "ms_per_call": mms,
+                        "tokens_per_s": w.B * 4 * 1e3 / mms},
     }
 
 

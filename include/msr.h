@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MSR_ABI_VERSION 1
+#define MSR_ABI_VERSION 2
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
 #define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
 #define MSR_MAX_DV 1024   /* d_v limit */
@@ -97,6 +97,12 @@ typedef struct {
     float gn_eps;            /* GroupNorm epsilon, >= 0 (1e-5 is the usual value) */
     int64_t pos0;            /* absolute position of token 0 (>= 0) for the rotation */
     uint32_t flags;          /* MSR_FLAG_* */
+    /* [device] B starting positions, one per batch row (8-byte aligned), or
+     * NULL: row b's token t is at position pos_rows[b] + t instead of pos0 + t.
+     * For batched serving, where each sequence is at its own position.  The
+     * values must be >= 0 and stay below 2^40 - T; they are not checked (they
+     * live on the device). */
+    const int64_t *pos_rows;
 } msr_problem;
 
 /* Library version check: returns MSR_ABI_VERSION. */
@@ -127,11 +133,12 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
                         size_t ws_bytes, void *hip_stream);
 
 /*
- * Chunkwise-recurrent form with chunk size `chunk` (1 <= chunk, chunk divides
- * T, else MSR_ERR_SHAPE) (jsqmd.com section 4.3; aiqz.cc "chunkwise
- * recurrence"): the intra-chunk parallel product plus the decayed state
- * carried across chunks, as in the header comment.  Same outputs and state
- * as msr_parallel up to rounding.
+ * Chunkwise-recurrent form with chunk size `chunk` >= 1 (jsqmd.com section
+ * 4.3; aiqz.cc "chunkwise recurrence"): the intra-chunk parallel product plus
+ * the decayed state carried across chunks, as in the header comment.  When
+ * chunk does not divide T the last chunk holds the remaining T mod chunk
+ * tokens (computed on the general-purpose path).  Same outputs and state as
+ * msr_parallel up to rounding, for any chunk.
  */
 msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
                          const void *V, void *O, const float *state_in, float *state_out,
@@ -139,8 +146,9 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
 
 /*
  * One recurrent decode step for every pair, p->T must be 1 and p->pos0 is
- * the absolute position of the token (jsqmd.com section 4.2; aiqz.cc
- * "recurrent representation"):
+ * the absolute position of the token (or p->pos_rows[b] that of batch row
+ * b's token, for sequences at different positions) (jsqmd.com section 4.2;
+ * aiqz.cc "recurrent representation"):
  *   state <- gamma state + k~^T v   (in place, fp32)
  *   o      = GN(q~ state)           (uses the updated state)
  * Needs no workspace.

@@ -291,7 +291,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
         float cc[4] = {1.f, 1.f, 1.f, 1.f}, ss[4] = {0.f, 0.f, 0.f, 0.f}, c1[4], s1[4];
         const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
         if (rot) {
-            const int64_t p0 = c.pos0 + (int64_t)ci * BC + r0;
+            const int64_t p0 = row_pos0(c, b) + (int64_t)ci * BC + r0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float th = c.theta[4 * c8 + i];

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(MsrConst c, const T
         const float q0 = load(q, qk_base + 2 * i), q1 = load(q, qk_base + 2 * i + 1);
         const float k0 = load(k, qk_base + 2 * i), k1 = load(k, qk_base + 2 * i + 1);
         float cs = 1.f, sn = 0.f;
-        if (!(c.flags & MSR_FLAG_NO_ROTATE)) rot_cos_sin(c.pos0, c.theta[i], cs, sn);
+        if (!(c.flags & MSR_FLAG_NO_ROTATE)) rot_cos_sin(row_pos0(c, pair / c.H), c.theta[i], cs, sn);
         qs[2 * i] = q0 * cs - q1 * sn;
         qs[2 * i + 1] = q1 * cs + q0 * sn;
         ks[2 * i] = (k0 * cs - k1 * sn) * c.scale;

@@ -32,7 +32,7 @@ __global__ void rotate_kernel(MsrConst c, const TIn *__restrict__ x, float *__re
         float y0 = x0, y1 = x1;
         if (!(c.flags & MSR_FLAG_NO_ROTATE)) {
             float cs, sn;
-            rot_cos_sin(c.pos0 + t, c.theta[i], cs, sn);
+            rot_cos_sin(row_pos0(c, b) + t, c.theta[i], cs, sn);
             y0 = x0 * cs - x1 * sn;
             y1 = x1 * cs + x0 * sn;
         }
@@ -57,30 +57,31 @@ __global__ __launch_bounds__(256) void generic_state_kernel(
     const size_t sidx = (static_cast<size_t>(pair) * c.dk + i) * c.dv + j;
     float S = (valid && s_in) ? s_in[sidx] : 0.f;
     const float lg = c.log2g[h];
-    const float gb = decay(static_cast<float>(chunk), lg);
-    const int nchunks = c.T / chunk;
+    // the last chunk holds T - (nchunks - 1) chunk tokens when chunk does not divide T
+    const int nchunks = (c.T + chunk - 1) / chunk;
     for (int ci = 0; ci < nchunks; ++ci) {
         if (chunk_states && valid)
             chunk_states[((static_cast<size_t>(pair) * nchunks + ci) * c.dk + i) * c.dv + j] = S;
+        const int len = min(chunk, c.T - ci * chunk);
         float acc = 0.f;
-        for (int t0 = 0; t0 < chunk; t0 += 16) {
+        for (int t0 = 0; t0 < len; t0 += 16) {
             const int tl = t0 + ty;
             const size_t tok = static_cast<size_t>(ci) * chunk + tl;
             const int ii = blockIdx.y * 16 + tx, jj = blockIdx.z * 16 + tx;
-            ks[ty][tx] = (tl < chunk && ii < c.dk)
+            ks[ty][tx] = (tl < len && ii < c.dk)
                              ? kr[(static_cast<size_t>(pair) * c.T + tok) * c.dk + ii] : 0.f;
-            vs[ty][tx] = (tl < chunk && jj < c.dv)
+            vs[ty][tx] = (tl < len && jj < c.dv)
                              ? load(v, ((static_cast<size_t>(b) * c.T + tok) * c.H + h) * c.dv + jj)
                              : 0.f;
             __syncthreads();
-            const int nt = min(16, chunk - t0);
+            const int nt = min(16, len - t0);
             for (int u = 0; u < nt; ++u) {
-                const float z = decay(static_cast<float>(chunk - 1 - (t0 + u)), lg);
+                const float z = decay(static_cast<float>(len - 1 - (t0 + u)), lg);
                 acc += z * ks[u][ty] * vs[u][tx];
             }
             __syncthreads();
         }
-        S = gb * S + acc;
+        S = decay(static_cast<float>(len), lg) * S + acc;
     }
     if (s_out && valid) s_out[sidx] = S;
 }

@@ -60,6 +60,8 @@ msr_status check_problem(const msr_problem *p, bool T1) {
     if (p->pos0 < 0) return fail(MSR_ERR_INVALID_ARG, "pos0=%lld must be >= 0", (long long)p->pos0);
     if (p->pos0 > ((int64_t)1 << 40) - p->T)
         return fail(MSR_ERR_INVALID_ARG, "positions beyond 2^40 are not supported");
+    if (p->pos_rows && (reinterpret_cast<uintptr_t>(p->pos_rows) & 7u))
+        return fail(MSR_ERR_INVALID_ARG, "pos_rows is not 8-byte aligned");
     if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM))
         return fail(MSR_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     return MSR_OK;
@@ -75,6 +77,7 @@ MsrConst make_const(const msr_problem *p, int chunk) {
     c.dv = p->dv;
     c.chunk = chunk;
     c.pos0 = p->pos0;
+    c.pos_rows = p->pos_rows;
     c.scale = p->scale != 0.f ? p->scale : (float)(1.0 / std::sqrt((double)p->dk));
     c.eps = p->gn_eps;
     c.flags = p->flags;
@@ -101,8 +104,8 @@ GenericPlan generic_plan(const msr_problem *p, int form, int chunk) {
     g.kr = round_up(tok);
     g.states = g.kr + round_up(tok);
     g.total = g.states;
-    if (form == MSR_FORM_CHUNKWISE && chunk > 0)
-        g.total += round_up((size_t)p->B * p->H * (p->T / chunk) * p->dk * p->dv * sizeof(float));
+    if (form == MSR_FORM_CHUNKWISE && chunk > 0)  // a partial last chunk counts as a chunk
+        g.total += round_up((size_t)p->B * p->H * ((p->T + chunk - 1) / chunk) * p->dk * p->dv * sizeof(float));
     return g;
 }
 
@@ -155,8 +158,7 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
         return MSR_OK;
     }
     if (form == MSR_FORM_CHUNKWISE) {
-        if (chunk < 1 || (p->T > 0 && p->T % chunk != 0))
-            return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1 and divide T=%d", chunk, p->T);
+        if (chunk < 1) return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1", chunk);
     } else if (form != MSR_FORM_PARALLEL) {
         return fail(MSR_ERR_INVALID_ARG, "unknown form %d", form);
     }
@@ -227,7 +229,7 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     char *w = static_cast<char *>(ws);
     float *qr = reinterpret_cast<float *>(w + g.qr), *kr = reinterpret_cast<float *>(w + g.kr);
     float *cs = reinterpret_cast<float *>(w + g.states);
-    const int64_t nchunks = p->T / chunk;
+    const int64_t nchunks = (p->T + chunk - 1) / chunk;
     hipError_t e = launch_rotate(c, p->dtype, Q, qr, 1.f, st);
     if (e == hipSuccess) e = launch_rotate(c, p->dtype, K, kr, c.scale, st);
     if (e == hipSuccess) e = launch_generic_state(c, p->dtype, chunk, kr, V, state_in, state_out, cs, st);

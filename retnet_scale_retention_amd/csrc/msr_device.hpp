@@ -44,6 +44,9 @@ __device__ __forceinline__ void rot_cos_sin(int64_t pos, float theta, float &cs,
     sincosf(static_cast<float>(r), &sn, &cs);
 }
 
+// position of token 0 of batch row b
+__device__ __forceinline__ int64_t row_pos0(const MsrConst &c, int b) { return c.pos_rows ? c.pos_rows[b] : c.pos0; }
+
 // gamma^d for d >= 0, as 2^(d * log2 gamma); never forms gamma^(-d).
 __device__ __forceinline__ float decay(float d, float log2g) { return exp2f(d * log2g); }
 

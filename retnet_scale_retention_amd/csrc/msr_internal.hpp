@@ -13,6 +13,7 @@ struct MsrConst {
     int32_t B, T, H, dk, dv;
     int32_t chunk;     // chunk size b (T for the parallel form)
     int64_t pos0;      // absolute position of token 0
+    const int64_t *pos_rows;  // device: per-batch-row start positions (NULL: pos0 for all)
     float scale;       // multiplies the rotated K
     float eps;         // GroupNorm epsilon
     uint32_t flags;    // MSR_FLAG_*

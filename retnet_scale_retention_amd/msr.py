@@ -40,6 +40,7 @@ class Problem(ctypes.Structure):
         ("gamma", ctypes.POINTER(ctypes.c_float)), ("theta", ctypes.POINTER(ctypes.c_float)),
         ("scale", ctypes.c_float), ("gn_eps", ctypes.c_float),
         ("pos0", ctypes.c_int64), ("flags", ctypes.c_uint32),
+        ("pos_rows", ctypes.c_void_p),
     ]
 
 
@@ -82,7 +83,8 @@ def _check(status: int):
 class _Desc:
     """A Problem plus the host arrays it points to (kept alive)."""
 
-    def __init__(self, B, T, H, dk, dv, dtype, gamma, theta=None, scale=0.0, eps=1e-5, pos0=0, flags=0):
+    def __init__(self, B, T, H, dk, dv, dtype, gamma, theta=None, scale=0.0, eps=1e-5, pos0=0, flags=0,
+                 pos_rows=None):
         self.gamma = np.ascontiguousarray(gamma, dtype=np.float32)
         if self.gamma.shape != (H,):
             raise ValueError(f"gamma must hold H={H} values")
@@ -92,7 +94,7 @@ class _Desc:
         fptr = lambda a: (ctypes.POINTER(ctypes.c_float)() if a is None
                           else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
         self.p = Problem(B, T, H, dk, dv, dtype, fptr(self.gamma), fptr(self.theta),
-                         float(scale), float(eps), int(pos0), int(flags))
+                         float(scale), float(eps), int(pos0), int(flags), pos_rows)
 
     @property
     def ref(self):
@@ -142,12 +144,23 @@ def _prep(q, k, v):
     return (*q.shape, v.shape[3])
 
 
+def _pos_rows(pos_rows, B, device):
+    """Device address of a per-batch-row position tensor (int64 [B]), or None."""
+    torch = _torch()
+    if pos_rows is None:
+        return None
+    if (pos_rows.dtype != torch.int64 or tuple(pos_rows.shape) != (B,) or not pos_rows.is_contiguous()
+            or pos_rows.device != device):
+        raise ValueError(f"pos_rows must be a contiguous int64 [B={B}] tensor on {device}")
+    return pos_rows.data_ptr()
+
+
 def _form(fn, form, q, k, v, gamma, chunk, theta, scale, eps, pos0, flags, state_in,
-          return_state, out, state_out, workspace, stream):
+          return_state, out, state_out, workspace, stream, pos_rows=None):
     torch = _torch()
     B, T, H, dk, dv = _prep(q, k, v)
     code = _dtype_code(q)
-    d = _Desc(B, T, H, dk, dv, code, gamma, theta, scale, eps, pos0, flags)
+    d = _Desc(B, T, H, dk, dv, code, gamma, theta, scale, eps, pos0, flags, _pos_rows(pos_rows, B, q.device))
     n = ctypes.c_size_t(0)
     _check(load().msr_workspace_size(d.ref, form, chunk, ctypes.byref(n)))
     if workspace is None or workspace.numel() < n.value:
@@ -170,25 +183,30 @@ def _form(fn, form, q, k, v, gamma, chunk, theta, scale, eps, pos0, flags, state
 
 def msr_parallel(q, k, v, gamma, *, theta=None, scale=0.0, eps=1e-5, pos0=0, flags=0,
                  state_in=None, return_state=True, out=None, state_out=None, workspace=None,
-                 stream=None):
+                 stream=None, pos_rows=None):
     """Parallel form. q, k: [B, T, H, dk]; v: [B, T, H, dv] (float32 or bfloat16,
-    on the device); gamma: H host values.  Returns (O, state_out or None)."""
+    on the device); gamma: H host values; pos_rows: optional int64 [B] device
+    tensor of per-row start positions (else every row starts at pos0).
+    Returns (O, state_out or None)."""
     return _form(load().msr_parallel, MSR_FORM_PARALLEL, q, k, v, gamma, 0, theta, scale, eps,
-                 pos0, flags, state_in, return_state, out, state_out, workspace, stream)
+                 pos0, flags, state_in, return_state, out, state_out, workspace, stream, pos_rows)
 
 
 def msr_chunkwise(q, k, v, gamma, chunk, *, theta=None, scale=0.0, eps=1e-5, pos0=0, flags=0,
                   state_in=None, return_state=True, out=None, state_out=None, workspace=None,
-                  stream=None):
-    """Chunkwise-recurrent form with chunk size `chunk` (must divide T)."""
+                  stream=None, pos_rows=None):
+    """Chunkwise-recurrent form with chunk size `chunk` (a last chunk shorter
+    than `chunk` takes the remaining tokens when chunk does not divide T)."""
     return _form(load().msr_chunkwise, MSR_FORM_CHUNKWISE, q, k, v, gamma, chunk, theta, scale,
-                 eps, pos0, flags, state_in, return_state, out, state_out, workspace, stream)
+                 eps, pos0, flags, state_in, return_state, out, state_out, workspace, stream, pos_rows)
 
 
 def msr_recurrent_step(q, k, v, state, gamma, pos, *, theta=None, scale=0.0, eps=1e-5, flags=0,
                        out=None, stream=None):
-    """One decode step at absolute position `pos`; q, k: [B, H, dk], v: [B, H, dv];
-    state [B, H, dk, dv] float32 is updated in place.  Returns o [B, H, dv]."""
+    """One decode step at absolute position `pos` (an int, or an int64 [B]
+    device tensor with one position per batch row); q, k: [B, H, dk],
+    v: [B, H, dv]; state [B, H, dk, dv] float32 is updated in place.
+    Returns o [B, H, dv]."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
         if not t.is_cuda or not t.is_contiguous():
@@ -197,7 +215,11 @@ def msr_recurrent_step(q, k, v, state, gamma, pos, *, theta=None, scale=0.0, eps
     dv = v.shape[2]
     if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
         raise ValueError("state must be float32 [B, H, dk, dv]")
-    d = _Desc(B, 1, H, dk, dv, _dtype_code(q), gamma, theta, scale, eps, pos, flags)
+    if isinstance(pos, torch.Tensor):
+        d = _Desc(B, 1, H, dk, dv, _dtype_code(q), gamma, theta, scale, eps, 0, flags,
+                  _pos_rows(pos, B, q.device))
+    else:
+        d = _Desc(B, 1, H, dk, dv, _dtype_code(q), gamma, theta, scale, eps, pos, flags)
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     _check(load().msr_recurrent_step(d.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),

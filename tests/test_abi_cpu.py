@@ -26,7 +26,15 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msr_abi_version() == 1
+    assert lib.msr_abi_version() == 2
+
+
+def test_problem_struct_layout_matches_the_header():
+    # the binding's struct mirrors msr_problem field by field (pos_rows last)
+    names = [f[0] for f in m.Problem._fields_]
+    assert names == ["B", "T", "H", "dk", "dv", "dtype", "gamma", "theta", "scale", "gn_eps", "pos0", "flags",
+                     "pos_rows"]
+    assert m.Problem.pos_rows.offset == 64 and ctypes.sizeof(m.Problem) == 72
 
 
 def desc(**kw):
@@ -58,11 +66,21 @@ def test_invalid_problems_are_rejected(kw, code):
     assert msr.load().msr_last_error().decode()
 
 
-def test_chunk_must_divide_T():
+def test_chunk_need_not_divide_T():
+    # a last chunk shorter than b takes the remaining tokens
     d = desc(T=96)
     assert status_ws(d, chunk=32)[0] == 0
-    assert m.STATUS[status_ws(d, chunk=40)[0]] == "MSR_ERR_SHAPE"
+    s40, n40 = status_ws(d, chunk=40)
+    s32, n32 = status_ws(d, chunk=32)
+    assert s40 == 0 and n40 > 0
     assert m.STATUS[status_ws(d, chunk=0)[0]] == "MSR_ERR_SHAPE"
+
+
+def test_misaligned_row_positions_are_rejected():
+    d = desc()
+    d.p.pos_rows = 0x10004  # 4-byte aligned only; never dereferenced
+    assert m.STATUS[status_ws(d)[0]] == "MSR_ERR_INVALID_ARG"
+    assert "pos_rows" in msr.load().msr_last_error().decode()
 
 
 def test_workspace_sizes_are_stable_and_step_needs_none():

@@ -1,0 +1,149 @@
+"""GPU parity of the batched-serving features: per-batch-row start
+positions (pos_rows), a last chunk shorter than b (b not dividing T), and
+multi-token decode steps carried through the state.  Each batch row is an
+independent sequence, so the reference is the fp64 oracle's plain parallel
+definition run on that row alone, at that row's start position.
+Tolerance as in the other parity tests: 1e-4 (fp32), 2e-2 (bf16)."""
+import numpy as np
+import pytest
+
+import msr_inputs as mi
+from oracle import oracle as orc
+from tests.gpu_util import TOL, down, note, out_err, state_err, torch_dev, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _msr():
+    import retnet_scale_retention_amd as msr
+    return msr
+
+
+def oracle_rows(q, k, v, g, pos, s_in=None):
+    """The oracle's parallel form, batch row b at start position pos[b]."""
+    outs, states = [], []
+    for b in range(q.shape[0]):
+        sb = None if s_in is None else s_in[b:b + 1]
+        o, s = orc.parallel(q[b:b + 1], k[b:b + 1], v[b:b + 1], g, pos0=int(pos[b]), s_in=sb)
+        outs.append(o)
+        states.append(s)
+    return np.concatenate(outs), np.concatenate(states)
+
+
+# (name, B, T, H, dk, dv, dtype, chunk): MFMA-path shapes and general-path shapes
+ROW_CASES = [
+    ("bf16-mfma-b64", 3, 256, 2, 64, 128, "bf16", 64),
+    ("bf16-mfma-b128", 2, 256, 2, 128, 64, "bf16", 128),
+    ("f32-general", 3, 48, 2, 16, 16, "f32", 16),
+]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=[c[0] for c in ROW_CASES])
+@pytest.mark.parametrize("form", ["chunkwise", "parallel"])
+def test_row_positions_vs_oracle(case, form):
+    name, B, T, H, dk, dv, dtype, chunk = case
+    torch, dev = torch_dev()
+    msr = _msr()
+    w = mi.Workload("rows-" + name, 40, B, T, H, dk, dv, dtype, (chunk,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    s_in = mi.state(w, 0.5)
+    pos = np.array([0, 1000, 37][:B], dtype=np.int64)
+    ro, rs = oracle_rows(q, k, v, g, pos, s_in)
+    qd, kd, vd = (up(x, dtype, dev) for x in (q, k, v))
+    sd = torch.from_numpy(s_in).to(dev)
+    pd = torch.from_numpy(pos).to(dev)
+    note(f"{name} {form}: positions {pos.tolist()}")
+    if form == "chunkwise":
+        o, s = msr.msr_chunkwise(qd, kd, vd, g, chunk, state_in=sd, pos_rows=pd)
+    else:
+        o, s = msr.msr_parallel(qd, kd, vd, g, state_in=sd, pos_rows=pd)
+    torch.cuda.synchronize()
+    eo, es = out_err(down(o), ro), state_err(down(s), rs)
+    note(f"  O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+    # the same call with pos_rows = pos0 everywhere equals the pos0 call
+    o2, _ = msr.msr_chunkwise(qd, kd, vd, g, chunk, state_in=sd, pos0=37,
+                              pos_rows=torch.full((B,), 37, dtype=torch.int64, device=dev))
+    o3, _ = msr.msr_chunkwise(qd, kd, vd, g, chunk, state_in=sd, pos0=37)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o3)
+
+
+# (name, B, T, H, dk, dv, dtype, chunk) with chunk not dividing T
+PARTIAL_CASES = [
+    ("bf16-T200-b64", 2, 200, 2, 64, 128, "bf16", 64),
+    ("bf16-T100-b128", 1, 100, 2, 128, 64, "bf16", 128),  # one chunk, shorter than b
+    ("f32-T50-b16", 1, 50, 2, 16, 16, "f32", 16),
+    ("f32-T7-b3", 2, 7, 1, 8, 8, "f32", 3),
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=[c[0] for c in PARTIAL_CASES])
+def test_partial_last_chunk_vs_oracle(case):
+    name, B, T, H, dk, dv, dtype, chunk = case
+    torch, dev = torch_dev()
+    msr = _msr()
+    w = mi.Workload("partial-" + name, 41, B, T, H, dk, dv, dtype, (chunk,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    s_in = mi.state(w, 0.5)
+    ro, rs = orc.parallel(q, k, v, g, s_in=s_in, pos0=5)
+    qd, kd, vd = (up(x, dtype, dev) for x in (q, k, v))
+    o, s = msr.msr_chunkwise(qd, kd, vd, g, chunk, state_in=torch.from_numpy(s_in).to(dev), pos0=5)
+    torch.cuda.synchronize()
+    eo, es = out_err(down(o), ro), state_err(down(s), rs)
+    note(f"{name}: O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+def test_ragged_decode_steps_vs_oracle():
+    """Single-token steps for sequences at different positions (one position
+    per batch row), state carried in place."""
+    torch, dev = torch_dev()
+    msr = _msr()
+    B, H, dk, dv, steps = 4, 2, 64, 128, 6
+    w = mi.Workload("ragged-decode", 42, B, steps, H, dk, dv, "bf16", (1,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    s_in = mi.state(w, 0.5)
+    pos = np.array([0, 17, 2048, 5], dtype=np.int64)
+    ro, rs = oracle_rows(q, k, v, g, pos, s_in)
+    st = torch.from_numpy(s_in).to(dev)
+    outs = []
+    for t in range(steps):
+        pd = torch.from_numpy(pos + t).to(dev)
+        o = msr.msr_recurrent_step(up(q[:, t], "bf16", dev).contiguous(), up(k[:, t], "bf16", dev).contiguous(),
+                                   up(v[:, t], "bf16", dev).contiguous(), st, g, pd)
+        outs.append(down(o))
+    torch.cuda.synchronize()
+    eo, es = out_err(np.stack(outs, 1), ro), state_err(down(st), rs)
+    note(f"ragged decode: O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("tokens_per_step", [1, 4, 16])
+def test_multi_token_steps_vs_oracle(tokens_per_step):
+    """Serving loop: each step feeds the next tokens_per_step tokens of every
+    sequence (rows at different positions) through msr_chunkwise with the
+    state carried; the outputs equal the oracle's single pass per row."""
+    torch, dev = torch_dev()
+    msr = _msr()
+    B, T, H, dk, dv = 3, 48, 2, 64, 128
+    w = mi.Workload("multi-step", 43, B, T, H, dk, dv, "bf16", (tokens_per_step,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    pos = np.array([3, 300, 0], dtype=np.int64)
+    ro, rs = oracle_rows(q, k, v, g, pos)
+    st = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
+    outs = []
+    for t0 in range(0, T, tokens_per_step):
+        sl = slice(t0, t0 + tokens_per_step)
+        qd, kd, vd = (up(np.ascontiguousarray(x[:, sl]), "bf16", dev) for x in (q, k, v))
+        pd = torch.from_numpy(pos + t0).to(dev)
+        o, _ = msr.msr_chunkwise(qd, kd, vd, g, tokens_per_step, state_in=st, state_out=st, pos_rows=pd)
+        outs.append(down(o))
+    torch.cuda.synchronize()
+    eo, es = out_err(np.concatenate(outs, 1), ro), state_err(down(st), rs)
+    note(f"{tokens_per_step} tokens per step: O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
