@@ -267,8 +267,8 @@ def bench_decode(torch, msr, mi, nsteps):
         "prefill_ms": prefill_ms,
         "ragged": {"note": "one position per batch row", "steps": nr, "kernel_us": rk * 1e3,
                    "steps_per_s": 1e3 / rk, "hbm_frac": bytes_step / (rk / 1e3) / 1e9 / HBM_PEAK_GBS},
-        "multi_token": {"note": "4 tokens per sequence per call, chunkwise b=4 on the general-purpose path, "
-                                "rows at their own positions", "calls": nm, "ms_per_call": mms,
+        "multi_token": {"note": "4 tokens per sequence per call (msr_chunkwise, b=4: one pass over the state "
+                                "for all 4 tokens), rows at their own positions", "calls": nm, "ms_per_call": mms,
                         "tokens_per_s": w.B * 4 * 1e3 / mms},
     }
 

@@ -187,6 +187,12 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
 
     if (mfma_supported(p, MSR_FORM_PARALLEL, p->T))
         return hip_status(mfma_parallel(c, p, Q, K, V, O, state_in, state_out, ws, st), "mfma parallel");
+    if (p->T <= MSR_DECODE_MAX_T) {  // a few tokens: the recurrence, one pass over the state
+        main_kernel_begin(st);
+        const hipError_t e = launch_decode(c, p->dtype, Q, K, V, O, state_in, state_out, st);
+        main_kernel_end(st);
+        return hip_status(e, "short parallel");
+    }
 
     const GenericPlan g = generic_plan(p, MSR_FORM_PARALLEL, p->T);
     char *w = static_cast<char *>(ws);
@@ -224,6 +230,12 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     if (mfma_supported(p, MSR_FORM_CHUNKWISE, chunk))
         return hip_status(mfma_chunkwise(c, p, chunk, Q, K, V, O, state_in, state_out, ws, st),
                           "mfma chunkwise");
+    if (p->T <= MSR_DECODE_MAX_T) {  // a few tokens: one pass over the state (the result is independent of b)
+        main_kernel_begin(st);
+        const hipError_t e = launch_decode(c, p->dtype, Q, K, V, O, state_in, state_out, st);
+        main_kernel_end(st);
+        return hip_status(e, "short chunkwise");
+    }
 
     const GenericPlan g = generic_plan(p, MSR_FORM_CHUNKWISE, chunk);
     char *w = static_cast<char *>(ws);
@@ -257,7 +269,7 @@ msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k
     const MsrConst c = make_const(p, 1);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     main_kernel_begin(st);
-    const hipError_t e = launch_decode(c, p->dtype, q, k, v, o, state, st);
+    const hipError_t e = launch_decode(c, p->dtype, q, k, v, o, state, state, st);
     main_kernel_end(st);
     return hip_status(e, "decode step");
 }

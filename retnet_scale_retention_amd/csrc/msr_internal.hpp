@@ -44,9 +44,12 @@ hipError_t launch_generic_output(const MsrConst &c, int dtype, int chunk, const 
                                  const float *Kr, const void *V, void *O, const float *states,
                                  int64_t pair_stride, int64_t chunk_stride, hipStream_t st);
 
-// Recurrent decode step, state updated in place.
+// Recurrent form over c.T <= MSR_DECODE_MAX_T tokens per pair with one pass
+// over the state: s_in (NULL: zeros) -> s_out (NULL: dropped; may equal
+// s_in).  The single-token decode step, and short chunkwise/parallel calls.
+constexpr int MSR_DECODE_MAX_T = 16;
 hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void *k,
-                         const void *v, void *o, float *state, hipStream_t st);
+                         const void *v, void *o, const float *s_in, float *s_out, hipStream_t st);
 
 // s_out = s_in (or zeros when s_in is NULL); used for T == 0.
 hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out, hipStream_t st);

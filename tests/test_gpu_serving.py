@@ -147,3 +147,32 @@ def test_multi_token_steps_vs_oracle(tokens_per_step):
     eo, es = out_err(np.concatenate(outs, 1), ro), state_err(down(st), rs)
     note(f"{tokens_per_step} tokens per step: O err {eo:.2e}  state err {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [2, 9, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("form", ["chunkwise", "parallel"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_short_calls_vs_oracle(T, dtype, form, with_state):
+    """Calls of at most 16 tokens run the recurrence in one pass over the
+    state (any b); separate state_in and state_out buffers."""
+    torch, dev = torch_dev()
+    msr = _msr()
+    B, H, dk, dv = 2, 3, 32, 64
+    w = mi.Workload(f"short-{T}-{dtype}", 44, B, T, H, dk, dv, dtype, (T,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    s_in = mi.state(w, 0.5) if with_state else None
+    ro, rs = orc.parallel(q, k, v, g, s_in=s_in, pos0=11)
+    qd, kd, vd = (up(x, dtype, dev) for x in (q, k, v))
+    sd = None if s_in is None else torch.from_numpy(s_in).to(dev)
+    if form == "chunkwise":
+        o, s = msr.msr_chunkwise(qd, kd, vd, g, 3, state_in=sd, pos0=11)
+    else:
+        o, s = msr.msr_parallel(qd, kd, vd, g, state_in=sd, pos0=11)
+    torch.cuda.synchronize()
+    eo, es = out_err(down(o), ro), state_err(down(s), rs)
+    note(f"T={T} {dtype} {form} state={with_state}: O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+    if sd is not None:  # the incoming state is left untouched
+        assert np.array_equal(down(sd), s_in.astype(np.float64))
