@@ -86,7 +86,7 @@ typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
 enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u };
 
 /* forms, for msr_workspace_size */
-enum { MSR_FORM_PARALLEL = 0, MSR_FORM_CHUNKWISE = 1, MSR_FORM_STEP = 2 };
+enum { MSR_FORM_PARALLEL = 0, MSR_FORM_CHUNKWISE = 1, MSR_FORM_STEP = 2, MSR_FORM_BACKWARD = 3 };
 
 typedef struct {
     int32_t B, T, H, dk, dv; /* dk even, 2..MSR_MAX_DK; dv 4..MSR_MAX_DV, multiple of 4 */
@@ -143,6 +143,25 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
 msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
                          const void *V, void *O, const float *state_in, float *state_out,
                          void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Backward pass of the chunkwise form (equivalently of the parallel form):
+ * the gradients of a loss L through the rotation, the scale, the retention
+ * products and GroupNorm (jsqmd.com sections 2, 4 and 5; aiqz.cc parallel and
+ * chunkwise representations, differentiated).  Given dO = dL/dO [B][T][H][dv]
+ * (dtype of Q) and dstate_out = dL/dstate_out [B][H][dk][dv] (fp32, NULL for
+ * zero), writes dQ, dK [B][T][H][dk] and dV [B][T][H][dv] (dtype of Q) and,
+ * when dstate_in is non-NULL, dL/dstate_in (fp32).  Q, K, V and state_in are
+ * the forward call's inputs (state_in NULL: zero); the forward activations
+ * are recomputed, nothing from the forward call is needed.  Arithmetic is
+ * fp32 for both dtypes.  Needs dv <= MSR_MAX_DK (else MSR_ERR_UNSUPPORTED)
+ * and a workspace of msr_workspace_size(p, MSR_FORM_BACKWARD, chunk) bytes.
+ * The outputs must not overlap the inputs or each other.
+ */
+msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
+                                  const void *V, const float *state_in, const void *dO,
+                                  const float *dstate_out, void *dQ, void *dK, void *dV, float *dstate_in,
+                                  void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
  * One recurrent decode step for every pair, p->T must be 1 and p->pos0 is

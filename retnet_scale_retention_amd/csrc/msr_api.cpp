@@ -128,6 +128,89 @@ msr_status hip_status(hipError_t e, const char *what) {
     return MSR_OK;
 }
 
+// The general-purpose chunkwise path (any shape, either dtype, any chunk):
+// rotation into fp32 copies, chunk-entry states, outputs.  ws holds
+// generic_plan(p, MSR_FORM_CHUNKWISE, chunk).total bytes.
+hipError_t generic_chunkwise(const msr_problem *p, int chunk, const void *Q, const void *K, const void *V, void *O,
+                             const float *state_in, float *state_out, void *ws, hipStream_t st) {
+    const MsrConst c = make_const(p, chunk);
+    const GenericPlan g = generic_plan(p, MSR_FORM_CHUNKWISE, chunk);
+    char *w = static_cast<char *>(ws);
+    float *qr = reinterpret_cast<float *>(w + g.qr), *kr = reinterpret_cast<float *>(w + g.kr);
+    float *cs = reinterpret_cast<float *>(w + g.states);
+    const int64_t nchunks = (p->T + chunk - 1) / chunk;
+    hipError_t e = launch_rotate(c, p->dtype, Q, qr, 1.f, st);
+    if (e == hipSuccess) e = launch_rotate(c, p->dtype, K, kr, c.scale, st);
+    if (e == hipSuccess) e = launch_generic_state(c, p->dtype, chunk, kr, V, state_in, state_out, cs, st);
+    if (e == hipSuccess) {
+        main_kernel_begin(st);
+        e = launch_generic_output(c, p->dtype, chunk, qr, kr, V, O, cs, nchunks * p->dk * p->dv,
+                                  (int64_t)p->dk * p->dv, st);
+        main_kernel_end(st);
+    }
+    return e;
+}
+
+// ---- backward pass ------------------------------------------------------------
+// The retention-only sub-problems of the backward pass: fp32, no rotation, no
+// GroupNorm, scale 1, dimensions d1 (queries and keys) and d2 (values).
+msr_problem retention_problem(const msr_problem *p, int d1, int d2) {
+    msr_problem r = *p;
+    r.dk = d1;
+    r.dv = d2;
+    r.dtype = MSR_F32;
+    r.theta = nullptr;
+    r.scale = 1.f;
+    r.pos0 = 0;
+    r.pos_rows = nullptr;
+    r.flags = MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM;
+    return r;
+}
+
+// workspace: fp32 token-major tensors (N = B T H rows) and states, then the
+// general path's own workspace for the largest of its four calls
+struct BackPlan {
+    size_t qf = 0, kf = 0, vf = 0, qr = 0, kr = 0, oraw = 0, g = 0, vrev = 0, grev = 0, qrrev = 0, krrev = 0,
+           dq = 0, dkrev = 0, dvrev = 0, tmp = 0, s1 = 0, s2 = 0, s3 = 0, gws = 0, total = 0;
+};
+
+BackPlan back_plan(const msr_problem *p, int chunk) {
+    BackPlan b;
+    const size_t N = (size_t)p->B * p->T * p->H, dk = p->dk, dv = p->dv;
+    const size_t st = round_up((size_t)p->B * p->H * dk * dv * sizeof(float));
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += round_up(bytes);
+        return o;
+    };
+    const bool copy = p->dtype != MSR_F32;  // fp32 inputs are used in place
+    b.qf = copy ? take(N * dk * 4) : 0;
+    b.kf = copy ? take(N * dk * 4) : 0;
+    b.vf = copy ? take(N * dv * 4) : 0;
+    b.qr = take(N * dk * 4);
+    b.kr = take(N * dk * 4);
+    b.oraw = take(N * dv * 4);
+    b.g = take(N * dv * 4);
+    b.vrev = take(N * dv * 4);
+    b.grev = take(N * dv * 4);
+    b.qrrev = take(N * dk * 4);
+    b.krrev = take(N * dk * 4);
+    b.dq = take(N * dk * 4);
+    b.dkrev = take(N * dk * 4);
+    b.dvrev = take(N * dv * 4);
+    b.tmp = take(N * dk * 4);
+    b.s1 = take(st);
+    b.s2 = take(st);
+    b.s3 = take(st);
+    msr_problem a = retention_problem(p, p->dk, p->dv), t = retention_problem(p, p->dv, p->dk);
+    const size_t g1 = generic_plan(&a, MSR_FORM_CHUNKWISE, chunk).total;
+    const size_t g2 = generic_plan(&t, MSR_FORM_CHUNKWISE, chunk).total;
+    b.gws = take(g1 > g2 ? g1 : g2);
+    b.total = off;
+    return b;
+}
+
 }  // namespace
 
 void main_kernel_begin(hipStream_t st) {
@@ -155,6 +238,13 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
     if (s != MSR_OK) return s;
     if (form == MSR_FORM_STEP) {
         *bytes = 0;
+        return MSR_OK;
+    }
+    if (form == MSR_FORM_BACKWARD) {
+        if (chunk < 1) return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1", chunk);
+        if (p->dv > MSR_MAX_DK)
+            return fail(MSR_ERR_UNSUPPORTED, "the backward pass needs dv <= %d (dv=%d)", MSR_MAX_DK, p->dv);
+        *bytes = back_plan(p, chunk).total;
         return MSR_OK;
     }
     if (form == MSR_FORM_CHUNKWISE) {
@@ -237,21 +327,95 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
         return hip_status(e, "short chunkwise");
     }
 
-    const GenericPlan g = generic_plan(p, MSR_FORM_CHUNKWISE, chunk);
-    char *w = static_cast<char *>(ws);
-    float *qr = reinterpret_cast<float *>(w + g.qr), *kr = reinterpret_cast<float *>(w + g.kr);
-    float *cs = reinterpret_cast<float *>(w + g.states);
-    const int64_t nchunks = (p->T + chunk - 1) / chunk;
-    hipError_t e = launch_rotate(c, p->dtype, Q, qr, 1.f, st);
-    if (e == hipSuccess) e = launch_rotate(c, p->dtype, K, kr, c.scale, st);
-    if (e == hipSuccess) e = launch_generic_state(c, p->dtype, chunk, kr, V, state_in, state_out, cs, st);
-    if (e == hipSuccess) {
-        main_kernel_begin(st);
-        e = launch_generic_output(c, p->dtype, chunk, qr, kr, V, O, cs,
-                                  nchunks * p->dk * p->dv, (int64_t)p->dk * p->dv, st);
-        main_kernel_end(st);
+    return hip_status(generic_chunkwise(p, chunk, Q, K, V, O, state_in, state_out, ws, st), "generic chunkwise");
+}
+
+msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
+                                  const void *V, const float *state_in, const void *dO,
+                                  const float *dstate_out, void *dQ, void *dK, void *dV, float *dstate_in,
+                                  void *ws, size_t ws_bytes, void *hip_stream) {
+    msr_status s = check_problem(p, false);
+    if (s != MSR_OK) return s;
+    size_t need = 0;
+    if ((s = msr_workspace_size(p, MSR_FORM_BACKWARD, chunk, &need)) != MSR_OK) return s;
+    const bool any = (size_t)p->B * p->T > 0;
+    if (any && (!Q || !K || !V || !dO || !dQ || !dK || !dV))
+        return fail(MSR_ERR_INVALID_ARG, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
+    const void *ptrs[10] = {Q, K, V, state_in, dO, dstate_out, dQ, dK, dV, dstate_in};
+    const char *names[10] = {"Q", "K", "V", "state_in", "dO", "dstate_out", "dQ", "dK", "dV", "dstate_in"};
+    for (int i = 0; i < 10; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(MSR_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    for (int i = 6; i < 10; ++i)
+        for (int j = 0; j < 10; ++j)
+            if (i != j && ptrs[i] && ptrs[i] == ptrs[j])
+                return fail(MSR_ERR_INVALID_ARG, "%s must not alias %s", names[i], names[j]);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(MSR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+    if (ws && !aligned16(ws)) return fail(MSR_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const MsrConst c = make_const(p, chunk);
+    if (p->B == 0) return MSR_OK;
+    const int dk = p->dk, dv = p->dv, B = p->B, T = p->T, H = p->H;
+    if (T == 0) {  // state_out = state_in: dstate_in = dstate_out
+        if (!dstate_in) return MSR_OK;
+        return hip_status(launch_state_op(c, dk, dv, dstate_out, dstate_in, 0, 0.f, st), "backward");
     }
-    return hip_status(e, "generic chunkwise");
+    const BackPlan b = back_plan(p, chunk);
+    char *w = static_cast<char *>(ws);
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
+    const size_t N = (size_t)B * T * H;
+    const bool copy = p->dtype != MSR_F32;
+    const float *qf = copy ? F(b.qf) : static_cast<const float *>(Q);
+    const float *kf = copy ? F(b.kf) : static_cast<const float *>(K);
+    const float *vf = copy ? F(b.vf) : static_cast<const float *>(V);
+    float *qr = F(b.qr), *kr = F(b.kr), *oraw = F(b.oraw), *g = F(b.g), *gws = F(b.gws);
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    if (copy) {
+        ok(launch_to_f32(p->dtype, N * dk, Q, F(b.qf), st));
+        ok(launch_to_f32(p->dtype, N * dk, K, F(b.kf), st));
+        ok(launch_to_f32(p->dtype, N * dv, V, F(b.vf), st));
+    }
+    // 1. forward outputs before GroupNorm, and G = dL/dO_raw
+    msr_problem pf = *p;
+    pf.dtype = MSR_F32;
+    pf.flags |= MSR_FLAG_NO_GROUPNORM;
+    ok(generic_chunkwise(&pf, chunk, qf, kf, vf, oraw, state_in, nullptr, gws, st));
+    if (!(p->flags & MSR_FLAG_NO_GROUPNORM))
+        ok(launch_gn_backward(p->dtype, N, dv, c.eps, oraw, dO, g, st));
+    else
+        ok(launch_to_f32(p->dtype, N * dv, dO, g, st));
+    // 2. rotated (and scaled) Q~, K~, token-major fp32
+    ok(launch_rotate_tok(c, qf, qr, MSR_F32, 1.f, 1.f, st));
+    ok(launch_rotate_tok(c, kf, kr, MSR_F32, c.scale, 1.f, st));
+    // 3. dq~ = Ret(G, V, K~; S_in^T)
+    const msr_problem pa = retention_problem(p, dv, dk), pc = retention_problem(p, dk, dv);
+    float *sinT = state_in ? F(b.s1) : nullptr;
+    if (state_in) ok(launch_state_op(c, dk, dv, state_in, sinT, 1, 0.f, st));
+    ok(generic_chunkwise(&pa, chunk, g, vf, kr, F(b.dq), sinT, nullptr, gws, st));
+    // 4. the same tensors backward in time
+    ok(launch_reverse(B, T, H, dv, vf, F(b.vrev), MSR_F32, st));
+    ok(launch_reverse(B, T, H, dv, g, F(b.grev), MSR_F32, st));
+    ok(launch_reverse(B, T, H, dk, qr, F(b.qrrev), MSR_F32, st));
+    ok(launch_reverse(B, T, H, dk, kr, F(b.krrev), MSR_F32, st));
+    // 5. dk~ (reversed) = Ret(V, G, Q~; dS_out^T / gamma)
+    float *dsoT = dstate_out ? F(b.s2) : nullptr, *dso = dstate_out ? F(b.s3) : nullptr;
+    if (dstate_out) {
+        ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, st));
+        ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, st));
+    }
+    ok(generic_chunkwise(&pa, chunk, F(b.vrev), F(b.grev), F(b.qrrev), F(b.dkrev), dsoT, nullptr, gws, st));
+    // 6. dV (reversed) = Ret(K~, Q~, G; dS_out / gamma), whose outgoing state
+    //    times gamma is dS_in (s1 is free again: the first call has run)
+    float *sc = dstate_in ? F(b.s1) : nullptr;
+    ok(generic_chunkwise(&pc, chunk, F(b.krrev), F(b.qrrev), F(b.grev), F(b.dvrev), dso, sc, gws, st));
+    if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, st));
+    // 7. back through the rotation and the scale, into the caller's dtype
+    ok(launch_rotate_tok(c, F(b.dq), dQ, p->dtype, 1.f, -1.f, st));
+    ok(launch_reverse(B, T, H, dk, F(b.dkrev), F(b.tmp), MSR_F32, st));
+    ok(launch_rotate_tok(c, F(b.tmp), dK, p->dtype, c.scale, -1.f, st));
+    ok(launch_reverse(B, T, H, dv, F(b.dvrev), dV, p->dtype, st));
+    return hip_status(e, "backward");
 }
 
 msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k, const void *v,

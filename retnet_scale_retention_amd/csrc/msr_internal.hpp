@@ -54,6 +54,20 @@ hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void
 // s_out = s_in (or zeros when s_in is NULL); used for T == 0.
 hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out, hipStream_t st);
 
+// ---- backward-pass element-wise kernels (k_backward.hip) -------------------
+hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream_t st);
+// y = factor * R(sign * angle) x on token-major [B][T][H][dk] rows (y in out_dtype)
+hipError_t launch_rotate_tok(const MsrConst &c, const float *x, void *y, int out_dtype, float factor, float sign,
+                             hipStream_t st);
+// GroupNorm backward per row of dv values: x = the normalised input, dy (dtype) -> dx (fp32)
+hipError_t launch_gn_backward(int dtype, size_t rows, int dv, float eps, const float *x, const void *dy, float *dx,
+                              hipStream_t st);
+// time reversal of [B][T][H][d] (y in out_dtype)
+hipError_t launch_reverse(int B, int T, int H, int d, const float *x, void *y, int out_dtype, hipStream_t st);
+// out = gamma_h^power * in (transposed when transpose != 0), states [B][H][d1][d2]; in NULL -> zeros
+hipError_t launch_state_op(const MsrConst &c, int d1, int d2, const float *in, float *out, int transpose,
+                           float power, hipStream_t st);
+
 // Measurement hook (msr_set_kernel_events): records the caller's events
 // around the main kernel of a call on its stream.  No-ops when unset.
 void main_kernel_begin(hipStream_t st);

@@ -19,12 +19,12 @@ LIB_PATH = Path(os.environ.get("MSR_LIB", Path(__file__).resolve().parent / "lib
 MSR_OK = 0
 MSR_F32, MSR_BF16 = 0, 1
 MSR_FLAG_NO_ROTATE, MSR_FLAG_NO_GROUPNORM = 1, 2
-MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP = 0, 1, 2
+MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_ERR_DTYPE",
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
 EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_parallel",
-           "msr_chunkwise", "msr_recurrent_step", "msr_set_kernel_events")
+           "msr_chunkwise", "msr_chunkwise_backward", "msr_recurrent_step", "msr_set_kernel_events")
 
 
 class MsrError(RuntimeError):
@@ -66,6 +66,9 @@ def load():
     lib.msr_parallel.restype = ctypes.c_int
     lib.msr_chunkwise.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msr_chunkwise.restype = ctypes.c_int
+    lib.msr_chunkwise_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
+    lib.msr_chunkwise_backward.restype = ctypes.c_int
     lib.msr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.msr_recurrent_step.restype = ctypes.c_int
     lib.msr_set_kernel_events.argtypes = [vp, vp]
@@ -199,6 +202,35 @@ def msr_chunkwise(q, k, v, gamma, chunk, *, theta=None, scale=0.0, eps=1e-5, pos
     than `chunk` takes the remaining tokens when chunk does not divide T)."""
     return _form(load().msr_chunkwise, MSR_FORM_CHUNKWISE, q, k, v, gamma, chunk, theta, scale,
                  eps, pos0, flags, state_in, return_state, out, state_out, workspace, stream, pos_rows)
+
+
+def msr_chunkwise_backward(q, k, v, gamma, chunk, grad_out, *, grad_state=None, state_in=None, theta=None,
+                           scale=0.0, eps=1e-5, pos0=0, flags=0, pos_rows=None, want_state_grad=True,
+                           workspace=None, stream=None):
+    """Gradients of the chunkwise (= parallel) form through rotation, scale,
+    retention and GroupNorm.  grad_out: dL/dO [B, T, H, dv] (dtype of q);
+    grad_state: dL/dstate_out [B, H, dk, dv] float32 or None.  Returns
+    (dQ, dK, dV, dstate_in or None), dQ/dK/dV in the dtype of q."""
+    torch = _torch()
+    B, T, H, dk, dv = _prep(q, k, v)
+    if tuple(grad_out.shape) != (B, T, H, dv) or grad_out.dtype != q.dtype or not grad_out.is_contiguous():
+        raise ValueError("grad_out must be a contiguous [B, T, H, dv] tensor of q's dtype")
+    for name, t in (("state_in", state_in), ("grad_state", grad_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv)):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, dk, dv] tensor")
+    d = _Desc(B, T, H, dk, dv, _dtype_code(q), gamma, theta, scale, eps, pos0, flags,
+              _pos_rows(pos_rows, B, q.device))
+    n = ctypes.c_size_t(0)
+    _check(load().msr_workspace_size(d.ref, MSR_FORM_BACKWARD, chunk, ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if want_state_grad else None
+    _check(load().msr_chunkwise_backward(d.ref, int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(state_in),
+                                         _ptr(grad_out), _ptr(grad_state), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                                         _ptr(ds), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                         _stream(q, stream)))
+    return dq, dk_, dv_, ds
 
 
 def msr_recurrent_step(q, k, v, state, gamma, pos, *, theta=None, scale=0.0, eps=1e-5, flags=0,

@@ -1,0 +1,70 @@
+"""GPU parity of the backward pass (msr_chunkwise_backward) against the
+oracle's gradients (oracle/grad.py: the parallel definition in float64,
+differentiated by autograd; pinned to finite differences of the C oracle).
+Loss L = sum(O * dO) + sum(S_out * dS_out).  Tolerance as for the forward:
+max relative error per (batch, head) slice 1e-4 for fp32 inputs, 2e-2 for
+bf16 inputs (gradients returned in bf16)."""
+import numpy as np
+import pytest
+
+import msr_inputs as mi
+from oracle import grad as og
+from tests.gpu_util import TOL, down, note, out_err, state_err, torch_dev, up
+
+pytestmark = pytest.mark.gpu
+
+# (name, B, T, H, dk, dv, dtype, chunk)
+CASES = [
+    ("f32-tiny", 1, 64, 2, 16, 16, "f32", 16),
+    ("f32-T50-b16", 2, 50, 2, 16, 32, "f32", 16),   # last chunk shorter than b
+    ("bf16-small", 2, 256, 2, 64, 128, "bf16", 64),
+    ("bf16-dk128", 1, 128, 2, 128, 64, "bf16", 128),
+]
+
+
+def run(case, with_state, grad_state, flags=0, pos_rows=None, seed=50):
+    name, B, T, H, dk, dv, dtype, chunk = case
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    w = mi.Workload("bwd-" + name, seed, B, T, H, dk, dv, dtype, (chunk,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(H)
+    rng = np.random.default_rng(seed + 1)
+    do = mi.quantize(rng.standard_normal((B, T, H, dv)).astype(np.float32), dtype)
+    ds = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if grad_state else None
+    s_in = mi.state(w, 0.5) if with_state else None
+    kw = dict(rotate=not (flags & 1), groupnorm=not (flags & 2))
+    if pos_rows is not None:
+        kw["pos_rows"] = pos_rows
+    else:
+        kw["pos0"] = 3
+    ref = og.backward(q, k, v, g, do, grad_state=ds, s_in=s_in, **kw)
+    qd, kd, vd, dod = (up(x, dtype, dev) for x in (q, k, v, do))
+    t = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    pr = None if pos_rows is None else torch.tensor(pos_rows, dtype=torch.int64, device=dev)
+    got = msr.msr_chunkwise_backward(qd, kd, vd, g, chunk, dod, grad_state=t(ds), state_in=t(s_in),
+                                     flags=flags, pos0=3, pos_rows=pr)
+    torch.cuda.synchronize()
+    errs = [out_err(down(got[0]), ref[0]), out_err(down(got[1]), ref[1]), out_err(down(got[2]), ref[2]),
+            state_err(down(got[3]), ref[3])]
+    note(f"{name} state={with_state} dS={grad_state} flags={flags}: dQ {errs[0]:.2e} dK {errs[1]:.2e} "
+         f"dV {errs[2]:.2e} dS_in {errs[3]:.2e}")
+    return errs, TOL[dtype]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("with_state,grad_state", [(False, False), (True, True)])
+def test_backward_vs_oracle(case, with_state, grad_state):
+    errs, tol = run(case, with_state, grad_state)
+    assert max(errs) < tol
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])  # no rotation / no GroupNorm / neither
+def test_backward_flags_vs_oracle(flags):
+    errs, tol = run(CASES[0], True, True, flags=flags)
+    assert max(errs) < tol
+
+
+def test_backward_row_positions_vs_oracle():
+    errs, tol = run(CASES[2], True, False, pos_rows=[5, 700])
+    assert max(errs) < tol
