@@ -21,7 +21,7 @@ already resident in HBM.  The same JSON line also reports
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--copy-mib N]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -189,6 +189,38 @@ def bench_parallel(torch, msr, mi, steps):
             "kernel_mfma_frac": kflops / (kms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
+def bench_backward(torch, msr, mi, name, calls, chunk):
+    """The backward pass (msr_chunkwise_backward) on a workload: gradients of
+    L = sum(O dO) + sum(S_out dS_out) with respect to Q, K, V and S_in."""
+    w = mi.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    g = mi.gammas(w.H)
+    shp = lambda d: (w.B, w.T, w.H, d)
+    q = mi.device_normal(shp(w.dk), 4001, dev, torch.bfloat16)
+    k = mi.device_normal(shp(w.dk), 4002, dev, torch.bfloat16)
+    v = mi.device_normal(shp(w.dv), 4003, dev, torch.bfloat16)
+    do = mi.device_normal(shp(w.dv), 4004, dev, torch.bfloat16)
+    ds = mi.device_normal((w.B, w.H, w.dk, w.dv), 4005, dev, torch.float32)
+    ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_BACKWARD,
+                                        chunk), dtype=torch.uint8, device=dev)
+    msr.msr_chunkwise_backward(q, k, v, g, chunk, do, grad_state=ds, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(calls):
+        msr.msr_chunkwise_backward(q, k, v, g, chunk, do, grad_state=ds, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / calls
+    th = w.B * w.T * w.H
+    # algorithmic flops: three retention products, each (b+1)(d1+d2) + 4 d1 d2 per token-head
+    flops = th * (2 * ((chunk + 1) * (w.dv + w.dk) + 4 * w.dv * w.dk) + (chunk + 1) * (w.dk + w.dv) + 4 * w.dk * w.dv)
+    return {"config": {"workload": name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": chunk,
+                       "dtype": "bf16", "workspace_bytes": int(ws.numel())},
+            "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms / 1e3), "tflops": flops / (ms / 1e3) / 1e12}
+
+
 def bench_decode(torch, msr, mi, nsteps):
     w = mi.WORKLOADS["decode"]
     dev = torch.device("cuda:0")
@@ -302,6 +334,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -326,6 +359,10 @@ def main():
     w = r["workload"]
     dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
     par = None if args.no_parallel else bench_parallel(torch, msr, mi, 3)
+    bwd = None
+    if not args.no_backward:
+        bwd = {"small": bench_backward(torch, msr, mi, "small", 3, 64),
+               "7b": bench_backward(torch, msr, mi, "7b", 5, 128)}
     cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
@@ -358,6 +395,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": dec,
         "parallel": par,
+        "backward": bwd,
         "hbm_view": {"bytes_per_step": r["bytes"],
                      "achieved_GBs": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9,
                      "frac": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS},

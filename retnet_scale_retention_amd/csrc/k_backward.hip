@@ -25,78 +25,110 @@ __global__ void to_f32_kernel(size_t n, const TIn *__restrict__ x, float *__rest
 
 // y = factor * R(+-angle) x per channel pair of each [B][T][H][dk] row;
 // sign = +1: the forward rotation, -1: its inverse (the transpose).  TOut is
-// the destination element type.
-template <typename TOut>
-__global__ void rotate_tok_kernel(MsrConst c, const float *__restrict__ x, TOut *__restrict__ y, float factor,
-                                  float sign) {
+// the destination element type.  With ylo (bf16 destinations only), y gets
+// the bf16 rounding of each fp32 value and ylo the bf16 rounding of what
+// that leaves: y + ylo carries about 16 significant bits.
+template <typename TIn, typename TOut>
+__global__ void rotate_tok_kernel(MsrConst c, const TIn *__restrict__ x, TOut *__restrict__ y,
+                                  TOut *__restrict__ ylo, float factor, float sign) {
     const int half = c.dk / 2;
     const size_t n = (size_t)c.B * c.T * c.H * half;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
         const int i = (int)(e % half);
         const size_t r = e / half;  // (b T + t) H + h
         const int t = (int)((r / c.H) % c.T), b = (int)(r / ((size_t)c.H * c.T));
-        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+        const float x0 = load(x, 2 * e), x1 = load(x, 2 * e + 1);
         float cs = 1.f, sn = 0.f;
         if (!(c.flags & MSR_FLAG_NO_ROTATE)) rot_cos_sin(row_pos0(c, b) + t, c.theta[i], cs, sn);
         sn *= sign;
-        store(y, 2 * e, (x0 * cs - x1 * sn) * factor);
-        store(y, 2 * e + 1, (x1 * cs + x0 * sn) * factor);
+        const float a = (x0 * cs - x1 * sn) * factor, b2 = (x1 * cs + x0 * sn) * factor;
+        store(y, 2 * e, a);
+        store(y, 2 * e + 1, b2);
+        if constexpr (sizeof(TOut) == 2) {
+            if (ylo) {
+                store(ylo, 2 * e, a - bf16_to_f32(f32_to_bf16(a)));
+                store(ylo, 2 * e + 1, b2 - bf16_to_f32(f32_to_bf16(b2)));
+            }
+        }
     }
 }
 
 // GroupNorm backward, one wave per (token, head) row of d_v values:
 //   y = (x - mean) s,  s = 1/sqrt(var + eps),
 //   dx = s (dy - mean(dy) - y mean(dy y))
-template <typename TIn>
+template <typename TX, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void gn_backward_kernel(size_t rows, int dv, float eps,
-                                                          const float *__restrict__ x,
-                                                          const TIn *__restrict__ dy, float *__restrict__ dx) {
+                                                          const TX *__restrict__ x, const TIn *__restrict__ dy,
+                                                          TOut *__restrict__ dx) {
     const int lane = threadIdx.x & 63;
     const size_t row = blockIdx.x * (size_t)(blockDim.x / 64) + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const float *xr = x + row * dv;
+    const size_t r0 = row * dv;
     float s = 0.f;
-    for (int j = lane; j < dv; j += 64) s += xr[j];
+    for (int j = lane; j < dv; j += 64) s += load(x, r0 + j);
     const float mean = wave_sum(s) / dv;
     float q2 = 0.f;
-    for (int j = lane; j < dv; j += 64) q2 += (xr[j] - mean) * (xr[j] - mean);
+    for (int j = lane; j < dv; j += 64) {
+        const float d = load(x, r0 + j) - mean;
+        q2 += d * d;
+    }
     const float inv = 1.f / sqrtf(wave_sum(q2) / dv + eps);
+    auto yval = [&](int j) { return (load(x, r0 + j) - mean) * inv; };
     float sd = 0.f, sdy = 0.f;
     for (int j = lane; j < dv; j += 64) {
-        const float g = load(dy, row * dv + j);
+        const float g = load(dy, r0 + j);
         sd += g;
-        sdy += g * (xr[j] - mean) * inv;
+        sdy += g * yval(j);
     }
     const float md = wave_sum(sd) / dv, mdy = wave_sum(sdy) / dv;
-    for (int j = lane; j < dv; j += 64) {
-        const float yv = (xr[j] - mean) * inv;
-        dx[row * dv + j] = inv * (load(dy, row * dv + j) - md - yv * mdy);
-    }
+    for (int j = lane; j < dv; j += 64) store(dx, r0 + j, inv * (load(dy, r0 + j) - md - yval(j) * mdy));
 }
 
-// y[b][T-1-t][h][:] = x[b][t][h][:] (element type of y: TOut)
-template <typename TOut>
-__global__ void reverse_kernel(int B, int T, int H, int d, const float *__restrict__ x, TOut *__restrict__ y) {
-    const size_t row = (size_t)H * d, n = (size_t)B * T * row;
+// y[b][t'][h][0:len] = x[b][t][h][col0:col0+len] with t' = T-1-t when
+// reversing, else t: time reversal, a column slice, and dtype conversion
+template <typename TIn, typename TOut>
+__global__ void slice_kernel(int B, int T, int H, int d, int col0, int len, int reverse, const TIn *__restrict__ x,
+                             TOut *__restrict__ y) {
+    const size_t n = (size_t)B * T * H * len;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const size_t bt = e / row, w = e % row;
+        const int j = (int)(e % len);
+        const size_t r = e / len;  // (b T + t) H + h
+        const int h = (int)(r % H);
+        const size_t bt = r / H;
         const int t = (int)(bt % T);
         const size_t b = bt / T;
-        store(y, (b * T + (T - 1 - t)) * row + w, x[e]);
+        const size_t src = ((b * T + t) * H + h) * (size_t)d + col0 + j;
+        const size_t dst = ((b * T + (reverse ? T - 1 - t : t)) * H + h) * (size_t)len + j;
+        store(y, dst, load(x, src));
     }
 }
 
-// out[p][j][i] = f_h * in[p][i][j] (transpose = 1) or out[p][i][j] = f_h *
-// in[p][i][j] (transpose = 0), f_h = gamma_h^power; in NULL gives zeros
+// y (fp32) = x + (first ? 0 : y)
+template <typename TIn>
+__global__ void accumulate_kernel(size_t n, const TIn *__restrict__ x, float *__restrict__ y, int first) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        y[e] = load(x, e) + (first ? 0.f : y[e]);
+}
+
+// States in [B H][d1][d2], f_h = gamma_h^power, in NULL reads as zeros:
+//   transpose = 0: out[p][i][j] = f_h in[p][i][j]
+//   transpose = 1: out[p][j - j0][i] = f_h in[p][i][j] for j in [j0, j0 + nj)
+//                  (a row block of the transpose, [nj][d1] per pair)
 __global__ void state_kernel(MsrConst c, int d1, int d2, const float *__restrict__ in, float *__restrict__ out,
-                             int transpose, float power) {
-    const size_t per = (size_t)d1 * d2, n = (size_t)c.B * c.H * per;
+                             int transpose, float power, int j0, int nj) {
+    const size_t per_out = (size_t)d1 * (transpose ? nj : d2), n = (size_t)c.B * c.H * per_out;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const size_t p = e / per, w = e % per;
-        const int i = (int)(w / d2), j = (int)(w % d2);
+        const size_t p = e / per_out, w = e % per_out;
+        int i, j;
+        if (transpose) {
+            j = j0 + (int)(w / d1);
+            i = (int)(w % d1);
+        } else {
+            i = (int)(w / d2);
+            j = (int)(w % d2);
+        }
         const float f = exp2f(power * c.log2g[p % c.H]);
-        const float v = in ? in[e] * f : 0.f;
-        out[p * per + (transpose ? (size_t)j * d1 + i : w)] = v;
+        out[e] = in ? in[(p * d1 + i) * (size_t)d2 + j] * f : 0.f;
     }
 }
 
@@ -119,48 +151,90 @@ hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream
     return hipGetLastError();
 }
 
-hipError_t launch_rotate_tok(const MsrConst &c, const float *x, void *y, int out_dtype, float factor, float sign,
-                             hipStream_t st) {
+template <typename TIn>
+hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, int out_dtype, float factor,
+                         float sign, hipStream_t st) {
     const size_t n = (size_t)c.B * c.T * c.H * (c.dk / 2);
     if (n == 0) return hipSuccess;
     if (out_dtype == MSR_BF16)
-        hipLaunchKernelGGL(rotate_tok_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, c, x,
-                           static_cast<uint16_t *>(y), factor, sign);
+        hipLaunchKernelGGL((rotate_tok_kernel<TIn, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, c, x,
+                           static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign);
     else
-        hipLaunchKernelGGL(rotate_tok_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, c, x,
-                           static_cast<float *>(y), factor, sign);
+        hipLaunchKernelGGL((rotate_tok_kernel<TIn, float>), dim3(grid_for(n)), dim3(256), 0, st, c, x,
+                           static_cast<float *>(y), nullptr, factor, sign);
     return hipGetLastError();
 }
 
-hipError_t launch_gn_backward(int dtype, size_t rows, int dv, float eps, const float *x, const void *dy, float *dx,
-                              hipStream_t st) {
-    if (rows == 0) return hipSuccess;
+hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
+                             float sign, hipStream_t st, void *ylo) {
+    if (ylo && out_dtype != MSR_BF16) return hipErrorInvalidValue;
+    if (in_dtype == MSR_BF16)
+        return rotate_tok_in(c, static_cast<const uint16_t *>(x), y, ylo, out_dtype, factor, sign, st);
+    return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, st);
+}
+
+template <typename TX, typename TIn>
+hipError_t gn_backward_in(size_t rows, int dv, float eps, const TX *x, const TIn *dy, void *dx, int out_dtype,
+                          hipStream_t st) {
     const unsigned blocks = (unsigned)((rows + 3) / 4);
-    if (dtype == MSR_BF16)
-        hipLaunchKernelGGL(gn_backward_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st, rows, dv, eps, x,
-                           static_cast<const uint16_t *>(dy), dx);
+    if (out_dtype == MSR_BF16)
+        hipLaunchKernelGGL((gn_backward_kernel<TX, TIn, uint16_t>), dim3(blocks), dim3(256), 0, st, rows, dv, eps, x,
+                           dy, static_cast<uint16_t *>(dx));
     else
-        hipLaunchKernelGGL(gn_backward_kernel<float>, dim3(blocks), dim3(256), 0, st, rows, dv, eps, x,
-                           static_cast<const float *>(dy), dx);
+        hipLaunchKernelGGL((gn_backward_kernel<TX, TIn, float>), dim3(blocks), dim3(256), 0, st, rows, dv, eps, x,
+                           dy, static_cast<float *>(dx));
     return hipGetLastError();
 }
 
-hipError_t launch_reverse(int B, int T, int H, int d, const float *x, void *y, int out_dtype, hipStream_t st) {
-    const size_t n = (size_t)B * T * H * d;
+hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int x_dtype, const void *dy,
+                              int dy_dtype, void *dx, int out_dtype, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const bool xb = x_dtype == MSR_BF16, yb = dy_dtype == MSR_BF16;
+    typedef const uint16_t *HB;
+    typedef const float *HF;
+    if (xb && yb) return gn_backward_in(rows, dv, eps, HB(x), HB(dy), dx, out_dtype, st);
+    if (xb) return gn_backward_in(rows, dv, eps, HB(x), HF(dy), dx, out_dtype, st);
+    if (yb) return gn_backward_in(rows, dv, eps, HF(x), HB(dy), dx, out_dtype, st);
+    return gn_backward_in(rows, dv, eps, HF(x), HF(dy), dx, out_dtype, st);
+}
+
+template <typename TIn>
+hipError_t slice_in(int B, int T, int H, int d, int col0, int len, int reverse, const TIn *x, void *y, int out_dtype,
+                    hipStream_t st) {
+    const size_t n = (size_t)B * T * H * len;
     if (n == 0) return hipSuccess;
     if (out_dtype == MSR_BF16)
-        hipLaunchKernelGGL(reverse_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, B, T, H, d, x,
-                           static_cast<uint16_t *>(y));
+        hipLaunchKernelGGL((slice_kernel<TIn, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, B, T, H, d, col0, len,
+                           reverse, x, static_cast<uint16_t *>(y));
     else
-        hipLaunchKernelGGL(reverse_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, B, T, H, d, x,
-                           static_cast<float *>(y));
+        hipLaunchKernelGGL((slice_kernel<TIn, float>), dim3(grid_for(n)), dim3(256), 0, st, B, T, H, d, col0, len,
+                           reverse, x, static_cast<float *>(y));
+    return hipGetLastError();
+}
+
+hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int reverse, const void *x, int in_dtype,
+                        void *y, int out_dtype, hipStream_t st) {
+    if (in_dtype == MSR_BF16)
+        return slice_in(B, T, H, d, col0, len, reverse, static_cast<const uint16_t *>(x), y, out_dtype, st);
+    return slice_in(B, T, H, d, col0, len, reverse, static_cast<const float *>(x), y, out_dtype, st);
+}
+
+hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, int first, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    if (in_dtype == MSR_BF16)
+        hipLaunchKernelGGL(accumulate_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, n,
+                           static_cast<const uint16_t *>(x), y, first);
+    else
+        hipLaunchKernelGGL(accumulate_kernel<float>, dim3(grid_for(n)), dim3(256), 0, st, n,
+                           static_cast<const float *>(x), y, first);
     return hipGetLastError();
 }
 
 hipError_t launch_state_op(const MsrConst &c, int d1, int d2, const float *in, float *out, int transpose,
-                           float power, hipStream_t st) {
-    const size_t n = (size_t)c.B * c.H * d1 * d2;
+                           float power, int j0, int nj, hipStream_t st) {
+    const size_t n = (size_t)c.B * c.H * d1 * (transpose ? nj : d2);
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(state_kernel, dim3(grid_for(n)), dim3(256), 0, st, c, d1, d2, in, out, transpose, power);
+    hipLaunchKernelGGL(state_kernel, dim3(grid_for(n)), dim3(256), 0, st, c, d1, d2, in, out, transpose, power, j0,
+                       nj);
     return hipGetLastError();
 }

@@ -211,6 +211,179 @@ BackPlan back_plan(const msr_problem *p, int chunk) {
     return b;
 }
 
+// The bf16 backward on the MFMA kernels.  The two products whose scores
+// contract over d_v (queries G or V, keys V or G) take d_v in parts of at
+// most 256 (the MFMA kernels' d_k range): the scores are sums over the
+// contraction, so the parts' outputs add up.
+constexpr int kMaxParts = 16;
+int dv_parts(int dv, int *off, int *len) {
+    int n = 0, o = 0;
+    while (o < dv && n < kMaxParts) {
+        const int r = dv - o, l = r >= 256 ? 256 : r >= 128 ? 128 : 64;
+        off[n] = o;
+        len[n] = l;
+        o += l;
+        ++n;
+    }
+    return o == dv ? n : -1;
+}
+
+msr_problem mfma_sub(const msr_problem *p, int d1, int d2) {
+    msr_problem r = retention_problem(p, d1, d2);
+    r.dtype = MSR_BF16;
+    return r;
+}
+
+bool mfma_backward_ok(const msr_problem *p, int chunk) {
+    if (p->dtype != MSR_BF16 || p->dv % 64 != 0) return false;
+    int off[kMaxParts], len[kMaxParts];
+    const int n = dv_parts(p->dv, off, len);
+    if (n < 1) return false;
+    msr_problem c = mfma_sub(p, p->dk, p->dv);
+    if (!mfma_supported(&c, MSR_FORM_CHUNKWISE, chunk)) return false;
+    for (int i = 0; i < n; ++i) {
+        msr_problem a = mfma_sub(p, len[i], p->dk);
+        if (!mfma_supported(&a, MSR_FORM_CHUNKWISE, chunk)) return false;
+    }
+    return true;
+}
+
+struct BackPlanM {
+    size_t oraw = 0, g = 0, qr = 0, kr = 0, ql = 0, kl = 0, qrrev = 0, krrev = 0, qlrev = 0, klrev = 0, grev = 0,
+           p1 = 0, p2 = 0, part = 0, acc = 0, tmp = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, mws = 0, total = 0;
+};
+
+BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
+    BackPlanM b;
+    const size_t N = (size_t)p->B * p->T * p->H, dk = p->dk, dv = p->dv;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += round_up(bytes);
+        return o;
+    };
+    b.oraw = take(N * dv * 2);
+    b.g = take(N * dv * 2);
+    b.qr = take(N * dk * 2);
+    b.kr = take(N * dk * 2);
+    b.ql = take(N * dk * 2);
+    b.kl = take(N * dk * 2);
+    b.qrrev = take(N * dk * 2);
+    b.krrev = take(N * dk * 2);
+    b.qlrev = take(N * dk * 2);
+    b.klrev = take(N * dk * 2);
+    b.grev = take(N * dv * 2);
+    b.p1 = take(N * 256 * 2);
+    b.p2 = take(N * 256 * 2);
+    b.part = take(N * dk * 2);
+    b.acc = take(N * (dk > dv ? dk : dv) * 4);
+    b.tmp = take(N * dk * 4);
+    const size_t sp = (size_t)p->B * p->H * 256 * dk * 4, sf = (size_t)p->B * p->H * dk * dv * 4;
+    b.s1 = take(sp);
+    b.s2 = take(sp);
+    b.s3 = take(sf);
+    b.s4 = take(sf);
+    size_t m = mfma_workspace_bytes(p, MSR_FORM_CHUNKWISE, chunk);
+    msr_problem c = mfma_sub(p, p->dk, p->dv);
+    if (mfma_workspace_bytes(&c, MSR_FORM_CHUNKWISE, chunk) > m) m = mfma_workspace_bytes(&c, MSR_FORM_CHUNKWISE, chunk);
+    for (int l = 64; l <= 256; l *= 2) {
+        msr_problem a = mfma_sub(p, l, p->dk);
+        const size_t x = mfma_workspace_bytes(&a, MSR_FORM_CHUNKWISE, chunk);
+        if (x > m) m = x;
+    }
+    b.mws = take(m);
+    b.total = off;
+    return b;
+}
+
+// One retention call on the MFMA path (no rotation, no GroupNorm, scale 1).
+hipError_t mfma_ret(const msr_problem *sub, int chunk, const void *Q, const void *K, const void *V, void *O,
+                    const float *s_in, float *s_out, void *ws, hipStream_t st) {
+    const MsrConst c = make_const(sub, chunk);
+    return mfma_chunkwise(c, sub, chunk, Q, K, V, O, s_in, s_out, ws, st);
+}
+
+hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const void *K, const void *V,
+                         const float *state_in, const void *dO, const float *dstate_out, void *dQ, void *dK,
+                         void *dV, float *dstate_in, void *ws, hipStream_t st) {
+    const MsrConst c = make_const(p, chunk);
+    const BackPlanM b = back_plan_mfma(p, chunk);
+    char *w = static_cast<char *>(ws);
+    auto P = [&](size_t o) { return static_cast<void *>(w + o); };
+    auto F = [&](size_t o) { return reinterpret_cast<float *>(w + o); };
+    const int dk = p->dk, dv = p->dv, B = p->B, T = p->T, H = p->H;
+    const size_t N = (size_t)B * T * H;
+    const int BF = MSR_BF16;
+    int off[kMaxParts], len[kMaxParts];
+    const int np = dv_parts(dv, off, len);
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    const msr_problem pc = mfma_sub(p, dk, dv);
+    // 1. Q~ and K~ (scaled) as two-term bf16 splits hi + lo.  The score
+    //    products q~_n . k~_m go through hi.hi + lo.hi + hi.lo (retention is
+    //    linear in its queries and in its keys): a score much smaller than
+    //    |q~||k~| loses its relative accuracy when q~ and k~ are rounded to
+    //    bf16, and GroupNorm's backward amplifies that error on rows built
+    //    from few tokens.  Elsewhere Q~ and K~ enter as hi.
+    ok(launch_rotate_tok(c, Q, BF, P(b.qr), BF, 1.f, 1.f, st, P(b.ql)));
+    ok(launch_rotate_tok(c, K, BF, P(b.kr), BF, c.scale, 1.f, st, P(b.kl)));
+    // 2. outputs before GroupNorm in fp32 (three calls summed), then
+    //    G = dL/dO_raw (bf16) by GroupNorm's backward
+    const void *g = dO;
+    if (!(p->flags & MSR_FLAG_NO_GROUPNORM)) {
+        ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kr), V, P(b.oraw), state_in, nullptr, P(b.mws), st));
+        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 1, st));
+        ok(mfma_ret(&pc, chunk, P(b.ql), P(b.kr), V, P(b.oraw), state_in, nullptr, P(b.mws), st));
+        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
+        ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kl), V, P(b.oraw), nullptr, nullptr, P(b.mws), st));
+        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
+        ok(launch_gn_backward(N, dv, c.eps, F(b.acc), MSR_F32, dO, BF, P(b.g), BF, st));
+        g = P(b.g);
+    }
+    // 3. dq~ = sum over the d_v parts of Ret(G_part, V_part, K~; S_in^T rows of the part)
+    for (int i = 0; i < np && e == hipSuccess; ++i) {
+        const msr_problem a = mfma_sub(p, len[i], dk);
+        ok(launch_slice(B, T, H, dv, off[i], len[i], 0, g, BF, P(b.p1), BF, st));
+        ok(launch_slice(B, T, H, dv, off[i], len[i], 0, V, BF, P(b.p2), BF, st));
+        float *sinT = state_in ? F(b.s1) : nullptr;
+        if (state_in) ok(launch_state_op(c, dk, dv, state_in, sinT, 1, 0.f, off[i], len[i], st));
+        ok(mfma_ret(&a, chunk, P(b.p1), P(b.p2), P(b.kr), P(b.part), sinT, nullptr, P(b.mws), st));
+        ok(launch_accumulate(N * dk, P(b.part), BF, F(b.acc), i == 0, st));
+    }
+    ok(launch_rotate_tok(c, F(b.acc), MSR_F32, dQ, BF, 1.f, -1.f, st));
+    // 4. dk~ (backward in time) = sum over parts of Ret(V_part, G_part, Q~; dS_out^T / gamma rows)
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.qr), BF, P(b.qrrev), BF, st));
+    for (int i = 0; i < np && e == hipSuccess; ++i) {
+        const msr_problem a = mfma_sub(p, len[i], dk);
+        ok(launch_slice(B, T, H, dv, off[i], len[i], 1, V, BF, P(b.p1), BF, st));
+        ok(launch_slice(B, T, H, dv, off[i], len[i], 1, g, BF, P(b.p2), BF, st));
+        float *dsoT = dstate_out ? F(b.s2) : nullptr;
+        if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, off[i], len[i], st));
+        ok(mfma_ret(&a, chunk, P(b.p1), P(b.p2), P(b.qrrev), P(b.part), dsoT, nullptr, P(b.mws), st));
+        ok(launch_accumulate(N * dk, P(b.part), BF, F(b.acc), i == 0, st));
+    }
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, F(b.acc), MSR_F32, F(b.tmp), MSR_F32, st));
+    ok(launch_rotate_tok(c, F(b.tmp), MSR_F32, dK, BF, c.scale, -1.f, st));
+    // 5. dV (backward in time) = Ret(K~, Q~, G; dS_out / gamma), its scores
+    //    split as in 1. (summed in fp32); the first call's outgoing state
+    //    times gamma is dS_in
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kr), BF, P(b.krrev), BF, st));
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kl), BF, P(b.klrev), BF, st));
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.ql), BF, P(b.qlrev), BF, st));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, g, BF, P(b.grev), BF, st));
+    float *dso = dstate_out ? F(b.s3) : nullptr, *sc = dstate_in ? F(b.s4) : nullptr;
+    if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, 0, dv, st));
+    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, sc, P(b.mws), st));
+    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 1, st));
+    ok(mfma_ret(&pc, chunk, P(b.klrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, nullptr, P(b.mws), st));
+    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
+    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qlrev), P(b.grev), P(b.oraw), nullptr, nullptr, P(b.mws), st));
+    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, F(b.acc), MSR_F32, dV, BF, st));
+    if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, 0, dv, st));
+    return e;
+}
+
 }  // namespace
 
 void main_kernel_begin(hipStream_t st) {
@@ -244,7 +417,7 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
         if (chunk < 1) return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1", chunk);
         if (p->dv > MSR_MAX_DK)
             return fail(MSR_ERR_UNSUPPORTED, "the backward pass needs dv <= %d (dv=%d)", MSR_MAX_DK, p->dv);
-        *bytes = back_plan(p, chunk).total;
+        *bytes = mfma_backward_ok(p, chunk) ? back_plan_mfma(p, chunk).total : back_plan(p, chunk).total;
         return MSR_OK;
     }
     if (form == MSR_FORM_CHUNKWISE) {
@@ -358,8 +531,11 @@ msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const voi
     const int dk = p->dk, dv = p->dv, B = p->B, T = p->T, H = p->H;
     if (T == 0) {  // state_out = state_in: dstate_in = dstate_out
         if (!dstate_in) return MSR_OK;
-        return hip_status(launch_state_op(c, dk, dv, dstate_out, dstate_in, 0, 0.f, st), "backward");
+        return hip_status(launch_state_op(c, dk, dv, dstate_out, dstate_in, 0, 0.f, 0, dv, st), "backward");
     }
+    if (mfma_backward_ok(p, chunk))
+        return hip_status(backward_mfma(p, chunk, Q, K, V, state_in, dO, dstate_out, dQ, dK, dV, dstate_in, ws, st),
+                          "backward (mfma)");
     const BackPlan b = back_plan(p, chunk);
     char *w = static_cast<char *>(ws);
     auto F = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
@@ -382,39 +558,39 @@ msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const voi
     pf.flags |= MSR_FLAG_NO_GROUPNORM;
     ok(generic_chunkwise(&pf, chunk, qf, kf, vf, oraw, state_in, nullptr, gws, st));
     if (!(p->flags & MSR_FLAG_NO_GROUPNORM))
-        ok(launch_gn_backward(p->dtype, N, dv, c.eps, oraw, dO, g, st));
+        ok(launch_gn_backward(N, dv, c.eps, oraw, MSR_F32, dO, p->dtype, g, MSR_F32, st));
     else
         ok(launch_to_f32(p->dtype, N * dv, dO, g, st));
     // 2. rotated (and scaled) Q~, K~, token-major fp32
-    ok(launch_rotate_tok(c, qf, qr, MSR_F32, 1.f, 1.f, st));
-    ok(launch_rotate_tok(c, kf, kr, MSR_F32, c.scale, 1.f, st));
+    ok(launch_rotate_tok(c, qf, MSR_F32, qr, MSR_F32, 1.f, 1.f, st));
+    ok(launch_rotate_tok(c, kf, MSR_F32, kr, MSR_F32, c.scale, 1.f, st));
     // 3. dq~ = Ret(G, V, K~; S_in^T)
     const msr_problem pa = retention_problem(p, dv, dk), pc = retention_problem(p, dk, dv);
     float *sinT = state_in ? F(b.s1) : nullptr;
-    if (state_in) ok(launch_state_op(c, dk, dv, state_in, sinT, 1, 0.f, st));
+    if (state_in) ok(launch_state_op(c, dk, dv, state_in, sinT, 1, 0.f, 0, dv, st));
     ok(generic_chunkwise(&pa, chunk, g, vf, kr, F(b.dq), sinT, nullptr, gws, st));
     // 4. the same tensors backward in time
-    ok(launch_reverse(B, T, H, dv, vf, F(b.vrev), MSR_F32, st));
-    ok(launch_reverse(B, T, H, dv, g, F(b.grev), MSR_F32, st));
-    ok(launch_reverse(B, T, H, dk, qr, F(b.qrrev), MSR_F32, st));
-    ok(launch_reverse(B, T, H, dk, kr, F(b.krrev), MSR_F32, st));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, vf, MSR_F32, F(b.vrev), MSR_F32, st));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, g, MSR_F32, F(b.grev), MSR_F32, st));
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, qr, MSR_F32, F(b.qrrev), MSR_F32, st));
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, kr, MSR_F32, F(b.krrev), MSR_F32, st));
     // 5. dk~ (reversed) = Ret(V, G, Q~; dS_out^T / gamma)
     float *dsoT = dstate_out ? F(b.s2) : nullptr, *dso = dstate_out ? F(b.s3) : nullptr;
     if (dstate_out) {
-        ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, st));
-        ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, st));
+        ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, 0, dv, st));
+        ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, 0, dv, st));
     }
     ok(generic_chunkwise(&pa, chunk, F(b.vrev), F(b.grev), F(b.qrrev), F(b.dkrev), dsoT, nullptr, gws, st));
     // 6. dV (reversed) = Ret(K~, Q~, G; dS_out / gamma), whose outgoing state
     //    times gamma is dS_in (s1 is free again: the first call has run)
     float *sc = dstate_in ? F(b.s1) : nullptr;
     ok(generic_chunkwise(&pc, chunk, F(b.krrev), F(b.qrrev), F(b.grev), F(b.dvrev), dso, sc, gws, st));
-    if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, st));
+    if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, 0, dv, st));
     // 7. back through the rotation and the scale, into the caller's dtype
-    ok(launch_rotate_tok(c, F(b.dq), dQ, p->dtype, 1.f, -1.f, st));
-    ok(launch_reverse(B, T, H, dk, F(b.dkrev), F(b.tmp), MSR_F32, st));
-    ok(launch_rotate_tok(c, F(b.tmp), dK, p->dtype, c.scale, -1.f, st));
-    ok(launch_reverse(B, T, H, dv, F(b.dvrev), dV, p->dtype, st));
+    ok(launch_rotate_tok(c, F(b.dq), MSR_F32, dQ, p->dtype, 1.f, -1.f, st));
+    ok(launch_slice(B, T, H, dk, 0, dk, 1, F(b.dkrev), MSR_F32, F(b.tmp), MSR_F32, st));
+    ok(launch_rotate_tok(c, F(b.tmp), MSR_F32, dK, p->dtype, c.scale, -1.f, st));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, F(b.dvrev), MSR_F32, dV, p->dtype, st));
     return hip_status(e, "backward");
 }
 

@@ -55,18 +55,24 @@ hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void
 hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out, hipStream_t st);
 
 // ---- backward-pass element-wise kernels (k_backward.hip) -------------------
+// (every x / y below is an MSR_F32 or MSR_BF16 array as its *_dtype says)
 hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream_t st);
-// y = factor * R(sign * angle) x on token-major [B][T][H][dk] rows (y in out_dtype)
-hipError_t launch_rotate_tok(const MsrConst &c, const float *x, void *y, int out_dtype, float factor, float sign,
-                             hipStream_t st);
-// GroupNorm backward per row of dv values: x = the normalised input, dy (dtype) -> dx (fp32)
-hipError_t launch_gn_backward(int dtype, size_t rows, int dv, float eps, const float *x, const void *dy, float *dx,
-                              hipStream_t st);
-// time reversal of [B][T][H][d] (y in out_dtype)
-hipError_t launch_reverse(int B, int T, int H, int d, const float *x, void *y, int out_dtype, hipStream_t st);
-// out = gamma_h^power * in (transposed when transpose != 0), states [B][H][d1][d2]; in NULL -> zeros
+// y = factor * R(sign * angle) x on token-major [B][T][H][dk] rows; with ylo
+// (bf16 output only) y + ylo is a two-term bf16 split of the fp32 result
+hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
+                             float sign, hipStream_t st, void *ylo = nullptr);
+// GroupNorm backward per row of dv values: x = GroupNorm's input, dy = dL/d(output) -> dx
+hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int x_dtype, const void *dy,
+                              int dy_dtype, void *dx, int out_dtype, hipStream_t st);
+// y[b][t'][h][0:len] = x[b][t][h][col0:col0+len], t' = T-1-t when reverse
+hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int reverse, const void *x, int in_dtype,
+                        void *y, int out_dtype, hipStream_t st);
+// y = x + (first ? 0 : y), y fp32
+hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, int first, hipStream_t st);
+// states [B][H][d1][d2] scaled by gamma_h^power (in NULL -> zeros); transpose != 0 writes
+// rows j0..j0+nj-1 of the transpose ([nj][d1] per pair)
 hipError_t launch_state_op(const MsrConst &c, int d1, int d2, const float *in, float *out, int transpose,
-                           float power, hipStream_t st);
+                           float power, int j0, int nj, hipStream_t st);
 
 // Measurement hook (msr_set_kernel_events): records the caller's events
 // around the main kernel of a call on its stream.  No-ops when unset.

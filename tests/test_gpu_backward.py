@@ -19,6 +19,9 @@ CASES = [
     ("f32-T50-b16", 2, 50, 2, 16, 32, "f32", 16),   # last chunk shorter than b
     ("bf16-small", 2, 256, 2, 64, 128, "bf16", 64),
     ("bf16-dk128", 1, 128, 2, 128, 64, "bf16", 128),
+    ("bf16-dv512", 1, 256, 2, 64, 512, "bf16", 64),    # d_v in two parts of 256 on the MFMA path
+    ("bf16-dv320", 1, 128, 1, 128, 320, "bf16", 64),   # parts 256 + 64
+    ("bf16-T200", 1, 200, 2, 64, 128, "bf16", 64),     # b not dividing T: general path
 ]
 
 
@@ -60,11 +63,21 @@ def test_backward_vs_oracle(case, with_state, grad_state):
 
 
 @pytest.mark.parametrize("flags", [1, 2, 3])  # no rotation / no GroupNorm / neither
-def test_backward_flags_vs_oracle(flags):
-    errs, tol = run(CASES[0], True, True, flags=flags)
+@pytest.mark.parametrize("case", [CASES[0], CASES[2]], ids=["f32-general", "bf16-mfma"])
+def test_backward_flags_vs_oracle(case, flags):
+    errs, tol = run(case, True, True, flags=flags)
     assert max(errs) < tol
 
 
 def test_backward_row_positions_vs_oracle():
     errs, tol = run(CASES[2], True, False, pos_rows=[5, 700])
+    assert max(errs) < tol
+
+
+@pytest.mark.parametrize("seed", [51, 52, 53])
+@pytest.mark.parametrize("case", [CASES[2], CASES[3]], ids=["bf16-small", "bf16-dk128"])
+def test_backward_no_state_seeds(case, seed):
+    """Zero incoming state: the first tokens' pre-norm outputs are built from
+    few keys, where the gradients are most sensitive to score rounding."""
+    errs, tol = run(case, False, False, seed=seed)
     assert max(errs) < tol
