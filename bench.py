@@ -89,11 +89,21 @@ def chunk_bytes(T, H, B, dk, dv):
     return B * T * H * (2 * dk + 2 * dv) * 2
 
 
-def kernel_source_sha():
-    """Hash of the kernel sources and the build script (its flags shape the
-    generated code)."""
+# The sources each measured kernel is built from: its own file, the shared
+# device headers and the build script (whose flags shape the generated code).
+KERNEL_SOURCES = {
+    "chunk_mfma_kernel": "k_chunk_mfma.hip",
+    "prep_kernel": "k_chunk_mfma.hip",
+    "gn_finalize_kernel": "k_chunk_mfma.hip",
+    "decode_kernel": "k_decode.hip",
+}
+
+
+def kernel_source_sha(kernel):
+    """Hash of the sources `kernel` is built from."""
+    csrc = ROOT / "retnet_scale_retention_amd" / "csrc"
     h = hashlib.sha256()
-    for f in sorted((ROOT / "retnet_scale_retention_amd" / "csrc").glob("*")):
+    for f in [csrc / KERNEL_SOURCES[kernel]] + sorted(csrc.glob("*.hpp")):
         h.update(f.read_bytes())
     h.update((ROOT / "retnet_scale_retention_amd" / "build.py").read_bytes())
     return h.hexdigest()[:16]
@@ -101,12 +111,12 @@ def kernel_source_sha():
 
 def traffic_record(kernel):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE measurement, if it was taken on the current kernel sources."""
+    WRITE_SIZE measurement, if it was taken on the kernel's current sources."""
     p = ROOT / "profiles" / "traffic.json"
     if not p.exists():
         return None
     rec = json.loads(p.read_text()).get(kernel)
-    if not rec or rec.get("source_sha") != kernel_source_sha():
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
 

@@ -16,6 +16,47 @@ namespace {
 
 using namespace msr;
 
+// N contiguous elements (N = 1, 2, 4, 8; the address aligned to N elements)
+// to and from fp32, as one or two vector memory operations
+template <int N>
+__device__ __forceinline__ void ldv(const uint16_t *p, float (&v)[N]) {
+    typedef uint16_t V __attribute__((ext_vector_type(N)));
+    const V x = *reinterpret_cast<const V *>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = bf16_to_f32(x[i]);
+}
+template <int N>
+__device__ __forceinline__ void ldv(const float *p, float (&v)[N]) {
+    constexpr int M = N > 4 ? 4 : N;
+    typedef float V __attribute__((ext_vector_type(M)));
+#pragma unroll
+    for (int h = 0; h < N / M; ++h) {
+        const V x = *reinterpret_cast<const V *>(p + M * h);
+#pragma unroll
+        for (int i = 0; i < M; ++i) v[M * h + i] = x[i];
+    }
+}
+template <int N>
+__device__ __forceinline__ void stv(uint16_t *p, const float (&v)[N]) {
+    typedef uint16_t V __attribute__((ext_vector_type(N)));
+    V x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = f32_to_bf16(v[i]);
+    *reinterpret_cast<V *>(p) = x;
+}
+template <int N>
+__device__ __forceinline__ void stv(float *p, const float (&v)[N]) {
+    constexpr int M = N > 4 ? 4 : N;
+    typedef float V __attribute__((ext_vector_type(M)));
+#pragma unroll
+    for (int h = 0; h < N / M; ++h) {
+        V x;
+#pragma unroll
+        for (int i = 0; i < M; ++i) x[i] = v[M * h + i];
+        *reinterpret_cast<V *>(p + M * h) = x;
+    }
+}
+
 
 template <typename TIn>
 __global__ void to_f32_kernel(size_t n, const TIn *__restrict__ x, float *__restrict__ y) {
@@ -84,6 +125,43 @@ __global__ __launch_bounds__(256) void gn_backward_kernel(size_t rows, int dv, f
     for (int j = lane; j < dv; j += 64) store(dx, r0 + j, inv * (load(dy, r0 + j) - md - yval(j) * mdy));
 }
 
+// The same with the row held in registers: lane l owns elements
+// [PER l, PER l + PER) of a row of 64 PER values, read and written once.
+template <int PER, typename TX, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void gn_backward_row_kernel(size_t rows, float eps, const TX *__restrict__ x,
+                                                              const TIn *__restrict__ dy, TOut *__restrict__ dx) {
+    constexpr int dv = 64 * PER;
+    const int lane = threadIdx.x & 63;
+    const size_t row = blockIdx.x * (size_t)(blockDim.x / 64) + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const size_t r0 = row * dv + (size_t)PER * lane;
+    float xv[PER], gv[PER];
+    ldv<PER>(x + r0, xv);
+    ldv<PER>(dy + r0, gv);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s += xv[i];
+    const float mean = wave_sum(s) / dv;
+    float q2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        xv[i] -= mean;
+        q2 += xv[i] * xv[i];
+    }
+    const float inv = 1.f / sqrtf(wave_sum(q2) / dv + eps);
+    float sd = 0.f, sdy = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        xv[i] *= inv;  // y
+        sd += gv[i];
+        sdy += gv[i] * xv[i];
+    }
+    const float md = wave_sum(sd) / dv, mdy = wave_sum(sdy) / dv;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gv[i] = inv * (gv[i] - md - xv[i] * mdy);
+    stv<PER>(dx + r0, gv);
+}
+
 // y[b][t'][h][0:len] = x[b][t][h][col0:col0+len] with t' = T-1-t when
 // reversing, else t: time reversal, a column slice, and dtype conversion
 template <typename TIn, typename TOut>
@@ -103,11 +181,45 @@ __global__ void slice_kernel(int B, int T, int H, int d, int col0, int len, int 
     }
 }
 
+// The same, 8 consecutive elements per work item (d, col0, len multiples of 8)
+template <typename TIn, typename TOut>
+__global__ void slice8_kernel(int B, int T, int H, int d, int col0, int len, int reverse, const TIn *__restrict__ x,
+                              TOut *__restrict__ y) {
+    const int l8 = len / 8;
+    const size_t n = (size_t)B * T * H * l8;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const int j = (int)(e % l8) * 8;
+        const size_t r = e / l8;  // (b T + t) H + h
+        const int h = (int)(r % H);
+        const size_t bt = r / H;
+        const int t = (int)(bt % T);
+        const size_t b = bt / T;
+        float v[8];
+        ldv<8>(x + ((b * T + t) * H + h) * (size_t)d + col0 + j, v);
+        stv<8>(y + ((b * T + (reverse ? T - 1 - t : t)) * H + h) * (size_t)len + j, v);
+    }
+}
+
 // y (fp32) = x + (first ? 0 : y)
 template <typename TIn>
 __global__ void accumulate_kernel(size_t n, const TIn *__restrict__ x, float *__restrict__ y, int first) {
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
         y[e] = load(x, e) + (first ? 0.f : y[e]);
+}
+
+// the same, 8 elements per work item (n a multiple of 8)
+template <typename TIn>
+__global__ void accumulate8_kernel(size_t n8, const TIn *__restrict__ x, float *__restrict__ y, int first) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n8; e += (size_t)gridDim.x * blockDim.x) {
+        float a[8], b[8];
+        ldv<8>(x + 8 * e, a);
+        if (!first) {
+            ldv<8>(y + 8 * e, b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] += b[i];
+        }
+        stv<8>(y + 8 * e, a);
+    }
 }
 
 // States in [B H][d1][d2], f_h = gamma_h^power, in NULL reads as zeros:
@@ -173,9 +285,29 @@ hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, voi
     return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, st);
 }
 
+template <int PER, typename TX, typename TIn>
+hipError_t gn_backward_row(size_t rows, float eps, const TX *x, const TIn *dy, void *dx, int out_dtype,
+                           hipStream_t st) {
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    if (out_dtype == MSR_BF16)
+        hipLaunchKernelGGL((gn_backward_row_kernel<PER, TX, TIn, uint16_t>), dim3(blocks), dim3(256), 0, st, rows,
+                           eps, x, dy, static_cast<uint16_t *>(dx));
+    else
+        hipLaunchKernelGGL((gn_backward_row_kernel<PER, TX, TIn, float>), dim3(blocks), dim3(256), 0, st, rows, eps,
+                           x, dy, static_cast<float *>(dx));
+    return hipGetLastError();
+}
+
 template <typename TX, typename TIn>
 hipError_t gn_backward_in(size_t rows, int dv, float eps, const TX *x, const TIn *dy, void *dx, int out_dtype,
                           hipStream_t st) {
+    switch (dv) {  // rows of 64, 128, 256, 512 values: held in registers
+        case 64: return gn_backward_row<1>(rows, eps, x, dy, dx, out_dtype, st);
+        case 128: return gn_backward_row<2>(rows, eps, x, dy, dx, out_dtype, st);
+        case 256: return gn_backward_row<4>(rows, eps, x, dy, dx, out_dtype, st);
+        case 512: return gn_backward_row<8>(rows, eps, x, dy, dx, out_dtype, st);
+        default: break;
+    }
     const unsigned blocks = (unsigned)((rows + 3) / 4);
     if (out_dtype == MSR_BF16)
         hipLaunchKernelGGL((gn_backward_kernel<TX, TIn, uint16_t>), dim3(blocks), dim3(256), 0, st, rows, dv, eps, x,
@@ -203,6 +335,15 @@ hipError_t slice_in(int B, int T, int H, int d, int col0, int len, int reverse, 
                     hipStream_t st) {
     const size_t n = (size_t)B * T * H * len;
     if (n == 0) return hipSuccess;
+    if (d % 8 == 0 && col0 % 8 == 0 && len % 8 == 0) {
+        if (out_dtype == MSR_BF16)
+            hipLaunchKernelGGL((slice8_kernel<TIn, uint16_t>), dim3(grid_for(n / 8)), dim3(256), 0, st, B, T, H, d,
+                               col0, len, reverse, x, static_cast<uint16_t *>(y));
+        else
+            hipLaunchKernelGGL((slice8_kernel<TIn, float>), dim3(grid_for(n / 8)), dim3(256), 0, st, B, T, H, d,
+                               col0, len, reverse, x, static_cast<float *>(y));
+        return hipGetLastError();
+    }
     if (out_dtype == MSR_BF16)
         hipLaunchKernelGGL((slice_kernel<TIn, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, B, T, H, d, col0, len,
                            reverse, x, static_cast<uint16_t *>(y));
@@ -221,6 +362,15 @@ hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int rever
 
 hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, int first, hipStream_t st) {
     if (n == 0) return hipSuccess;
+    if (n % 8 == 0) {
+        if (in_dtype == MSR_BF16)
+            hipLaunchKernelGGL(accumulate8_kernel<uint16_t>, dim3(grid_for(n / 8)), dim3(256), 0, st, n / 8,
+                               static_cast<const uint16_t *>(x), y, first);
+        else
+            hipLaunchKernelGGL(accumulate8_kernel<float>, dim3(grid_for(n / 8)), dim3(256), 0, st, n / 8,
+                               static_cast<const float *>(x), y, first);
+        return hipGetLastError();
+    }
     if (in_dtype == MSR_BF16)
         hipLaunchKernelGGL(accumulate_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, n,
                            static_cast<const uint16_t *>(x), y, first);
