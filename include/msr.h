@@ -153,10 +153,14 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
  * zero), writes dQ, dK [B][T][H][dk] and dV [B][T][H][dv] (dtype of Q) and,
  * when dstate_in is non-NULL, dL/dstate_in (fp32).  Q, K, V and state_in are
  * the forward call's inputs (state_in NULL: zero); the forward activations
- * are recomputed, nothing from the forward call is needed.  Arithmetic is
- * fp32 for both dtypes.  Needs dv <= MSR_MAX_DK (else MSR_ERR_UNSUPPORTED)
- * and a workspace of msr_workspace_size(p, MSR_FORM_BACKWARD, chunk) bytes.
- * The outputs must not overlap the inputs or each other.
+ * are recomputed, nothing from the forward call is needed.  fp32 inputs
+ * (and bf16 shapes the matrix-core kernels do not take) run in fp32
+ * arithmetic; bf16 inputs with dv a multiple of 64 run the products as bf16
+ * matrix-core tiles with fp32 accumulation, the query-key scores from
+ * two-term bf16 splits of the rotated Q and K.  Needs dv <= MSR_MAX_DK (else
+ * MSR_ERR_UNSUPPORTED) and a workspace of
+ * msr_workspace_size(p, MSR_FORM_BACKWARD, chunk) bytes.  The outputs must not
+ * overlap the inputs or each other.
  */
 msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
                                   const void *V, const float *state_in, const void *dO,
