@@ -82,8 +82,19 @@ typedef enum {
 
 typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
 
-/* flags: switch parts of the operation off (used for staged checks) */
-enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u };
+/*
+ * flags.  NO_ROTATE and NO_GROUPNORM switch parts of the operation off (used
+ * for staged checks).  DECAY_ROWNORM normalises each row of the decay matrix
+ * to unit sum (jsqmd.com section 5, "normalisation strategy", which lists it
+ * among the score normalisations without a formula): the row of the token
+ * at absolute position p is divided by the sum of its decay weights over
+ * every position the sequence has reached, sum_{j=0}^{p} gamma^j =
+ * (1 - gamma^(p+1)) / (1 - gamma) (p + 1 when gamma = 1), so that a sequence
+ * split over several calls, its state carried, gives the same outputs as one
+ * call.  The factor multiplies the row's output before GroupNorm, which
+ * therefore sees it only through eps.
+ */
+enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u, MSR_FLAG_DECAY_ROWNORM = 4u };
 
 /* forms, for msr_workspace_size */
 enum { MSR_FORM_PARALLEL = 0, MSR_FORM_CHUNKWISE = 1, MSR_FORM_STEP = 2, MSR_FORM_BACKWARD = 3 };

@@ -29,6 +29,9 @@
  *                 article, the three forms)
  *   GroupNorm  -- one group per head over its d_v channels, per token
  *                 (jsqmd.com section 5; b99b.cn, retention features)
+ *   row-normalised decay (optional) -- each row of D divided by its sum
+ *                 (jsqmd.com section 5, one of the score normalisations it
+ *                 lists, no formula given)
  *
  * Readings where the pages are silent or garbled (the same readings the GPU
  * library implements, each justified in the design notes):
@@ -44,6 +47,10 @@
  *     gamma^(n+1) q_n S_in and the outgoing state is
  *     gamma^T S_in + sum_m gamma^(T-1-m) k_m^T v_m.
  *   - GroupNorm: biased variance, no affine, y = (x - mean)/sqrt(var + eps).
+ *   - Row-normalised decay: the row of the token at absolute position p
+ *     sums its decay weights over every position from 0 to p (the incoming
+ *     state stands for the positions before pos0), i.e. sum_{j=0}^{p}
+ *     gamma^j, and the row's output is divided by that sum before GroupNorm.
  *
  * Layouts (row-major, fp64): q, k [B][T][H][dk]; v, o [B][T][H][dv];
  * state [B][H][dk][dv].  Pairs (b, h) are independent and are spread over
@@ -66,6 +73,7 @@ typedef struct {
     int64_t pos0;        /* absolute position of token 0 */
     int rotate;          /* 0 => no rotation */
     int groupnorm;       /* 0 => raw retention output, no GroupNorm */
+    int rownorm;         /* 1 => row-normalised decay */
 } oracle_problem;
 
 int oracle_num_threads(void)
@@ -164,12 +172,32 @@ static void scratch_free(scratch *s)
     free(s->acc);
 }
 
+/* Sum of the decay weights of the row at absolute position pos: the
+ * weights gamma^(pos - m) of every position m = 0 .. pos, added one by one. */
+static double decay_row_sum(double g, int64_t pos)
+{
+    double s = 0.0;
+    for (int64_t m = 0; m <= pos; m++) s += pow(g, (double)(pos - m));
+    return s;
+}
+
+/* The finished output row of token t: the optional row normalisation of the
+ * decay (a factor on the whole row, state term included), then GroupNorm. */
+static void finish_row(const oracle_problem *p, double *row, int64_t pos, int h)
+{
+    if (p->rownorm) {
+        const double r = decay_row_sum(p->gamma[h], pos);
+        for (int j = 0; j < p->dv; j++) row[j] /= r;
+    }
+    if (p->groupnorm) groupnorm_row(row, p->dv, p->eps);
+}
+
 static void store_output(const oracle_problem *p, double *o, int b, int t, int h,
                          const double *acc)
 {
     double *dst = o + idx_tok(p, b, t, h, p->dv);
     memcpy(dst, acc, sizeof(double) * p->dv);
-    if (p->groupnorm) groupnorm_row(dst, p->dv, p->eps);
+    finish_row(p, dst, p->pos0 + t, h);
 }
 
 /*
@@ -391,7 +419,7 @@ int oracle_parallel_rows(const oracle_problem *p, int nrows, const int64_t *rows
                         acc[j] += gn * s;
                     }
                 }
-                if (p->groupnorm) groupnorm_row(acc, dv, p->eps);
+                finish_row(p, acc, p->pos0 + n, 0);
                 memcpy(o_rows + (size_t)r * dv, acc, sizeof(double) * dv);
             }
         }

@@ -51,6 +51,7 @@ class _Problem(ctypes.Structure):
         ("theta", ctypes.POINTER(ctypes.c_double)),
         ("scale", ctypes.c_double), ("eps", ctypes.c_double),
         ("pos0", ctypes.c_int64), ("rotate", ctypes.c_int), ("groupnorm", ctypes.c_int),
+        ("rownorm", ctypes.c_int),
     ]
 
 
@@ -110,7 +111,7 @@ def default_scale(dk: int) -> float:
 class _Call:
     """Marshals one problem description; keeps the fp64 buffers alive."""
 
-    def __init__(self, shape_q, dv, gamma, theta, scale, eps, pos0, rotate, groupnorm):
+    def __init__(self, shape_q, dv, gamma, theta, scale, eps, pos0, rotate, groupnorm, rownorm=False):
         B, T, H, dk = shape_q
         self.gamma = _f64(np.asarray(gamma, dtype=np.float32))
         if self.gamma.shape != (H,):
@@ -120,11 +121,11 @@ class _Call:
         sc = default_scale(dk) if scale is None else float(np.float32(scale))
         self.p = _Problem(B, T, H, dk, dv, _ptr(self.gamma), _ptr(self.theta), sc,
                           float(np.float32(eps)), int(pos0), int(bool(rotate)),
-                          int(bool(groupnorm)))
+                          int(bool(groupnorm)), int(bool(rownorm)))
 
 
 def _run(fn, q, k, v, gamma, *, chunk=None, theta=None, scale=None, eps=1e-5, pos0=0,
-         rotate=True, groupnorm=True, s_in=None, outputs=True, state=True):
+         rotate=True, groupnorm=True, rownorm=False, s_in=None, outputs=True, state=True):
     q, k, v, s_in = _f64(q), _f64(k), _f64(v), _f64(s_in)
     B, T, H, dk = q.shape
     dv = v.shape[3]
@@ -132,7 +133,7 @@ def _run(fn, q, k, v, gamma, *, chunk=None, theta=None, scale=None, eps=1e-5, po
         raise ValueError("q, k, v shapes disagree")
     if s_in is not None and s_in.shape != (B, H, dk, dv):
         raise ValueError("state shape must be [B, H, dk, dv]")
-    c = _Call(q.shape, dv, gamma, theta, scale, eps, pos0, rotate, groupnorm)
+    c = _Call(q.shape, dv, gamma, theta, scale, eps, pos0, rotate, groupnorm, rownorm)
     o = np.zeros((B, T, H, dv)) if outputs else None
     s_out = np.zeros((B, H, dk, dv)) if state else None
     lib = _load()
@@ -171,14 +172,14 @@ def step(q, k, v, state, gamma, pos, **kw):
 
 
 def parallel_rows(q, k, v, gamma, rows, *, theta=None, scale=None, eps=1e-5, pos0=0,
-                  rotate=True, groupnorm=True, s_in=None):
+                  rotate=True, groupnorm=True, rownorm=False, s_in=None):
     """Selected rows of the parallel definition for ONE (batch, head) pair.
     q, k: [T, dk]; v: [T, dv]; gamma: scalar; s_in: [dk, dv] or None.
     Returns [len(rows), dv]."""
     q, k, v, s_in = _f64(q), _f64(k), _f64(v), _f64(s_in)
     T, dk = q.shape
     dv = v.shape[1]
-    c = _Call((1, T, 1, dk), dv, [gamma], theta, scale, eps, pos0, rotate, groupnorm)
+    c = _Call((1, T, 1, dk), dv, [gamma], theta, scale, eps, pos0, rotate, groupnorm, rownorm)
     r = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.zeros((len(r), dv))
     rc = _load().oracle_parallel_rows(ctypes.byref(c.p), len(r),

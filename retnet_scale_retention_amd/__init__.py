@@ -1,7 +1,7 @@
 """MI355X-native multi-scale retention (RetNet MSR): parallel, chunkwise and
 recurrent-step forms as hand-written HIP kernels behind the C ABI of
 libmsr.so (include/msr.h).  This package is the thin Python binding."""
-from .msr import (MSR_BF16, MSR_F32, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_NO_ROTATE,  # noqa: F401
+from .msr import (MSR_BF16, MSR_F32, MSR_FLAG_DECAY_ROWNORM, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_NO_ROTATE,  # noqa: F401
                   MSR_FORM_BACKWARD, MSR_FORM_CHUNKWISE, MSR_FORM_PARALLEL, MSR_FORM_STEP, MsrError,
                   load, msr_chunkwise, msr_chunkwise_backward, msr_parallel, msr_recurrent_step,
                   set_kernel_events,

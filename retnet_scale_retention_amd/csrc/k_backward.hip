@@ -222,6 +222,18 @@ __global__ void accumulate8_kernel(size_t n8, const TIn *__restrict__ x, float *
     }
 }
 
+// Rows [B][T][H][d] times the row-normalised-decay factor at their absolute
+// positions (1 when the problem does not ask for it); y may be x
+template <typename TIn, typename TOut>
+__global__ void row_scale_kernel(MsrConst c, int d, const TIn *x, TOut *y) {
+    const size_t n = (size_t)c.B * c.T * c.H * d;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = e / d;  // (b T + t) H + h
+        const int h = (int)(r % c.H), t = (int)((r / c.H) % c.T), b = (int)(r / ((size_t)c.H * c.T));
+        store(y, e, load(x, e) * row_norm_factor(c, row_pos0(c, b) + t, c.log2g[h]));
+    }
+}
+
 // States in [B H][d1][d2], f_h = gamma_h^power, in NULL reads as zeros:
 //   transpose = 0: out[p][i][j] = f_h in[p][i][j]
 //   transpose = 1: out[p][j - j0][i] = f_h in[p][i][j] for j in [j0, j0 + nj)
@@ -358,6 +370,25 @@ hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int rever
     if (in_dtype == MSR_BF16)
         return slice_in(B, T, H, d, col0, len, reverse, static_cast<const uint16_t *>(x), y, out_dtype, st);
     return slice_in(B, T, H, d, col0, len, reverse, static_cast<const float *>(x), y, out_dtype, st);
+}
+
+hipError_t launch_row_scale(const MsrConst &c, int d, const void *x, int in_dtype, void *y, int out_dtype,
+                            hipStream_t st) {
+    const size_t n = (size_t)c.B * c.T * c.H * d;
+    if (n == 0) return hipSuccess;
+    typedef const uint16_t *HB;
+    typedef const float *HF;
+    typedef uint16_t *OB;
+    typedef float *OF;
+    if (in_dtype == MSR_BF16 && out_dtype == MSR_BF16)
+        hipLaunchKernelGGL((row_scale_kernel<uint16_t, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, c, d, HB(x), OB(y));
+    else if (in_dtype == MSR_BF16)
+        hipLaunchKernelGGL((row_scale_kernel<uint16_t, float>), dim3(grid_for(n)), dim3(256), 0, st, c, d, HB(x), OF(y));
+    else if (out_dtype == MSR_BF16)
+        hipLaunchKernelGGL((row_scale_kernel<float, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, c, d, HF(x), OB(y));
+    else
+        hipLaunchKernelGGL((row_scale_kernel<float, float>), dim3(grid_for(n)), dim3(256), 0, st, c, d, HF(x), OF(y));
+    return hipGetLastError();
 }
 
 hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, int first, hipStream_t st) {

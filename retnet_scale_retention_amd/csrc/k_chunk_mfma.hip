@@ -748,6 +748,11 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         for (int u = 0; u < C::NQT; ++u) {
             const int jq = 16 * qt[u] + l16;
             pend_row[u] = (uint32_t)(t0 + jq) * c.H + h;
+            if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+                const float f = 1.f / decay_row_sum(row_pos0(c, b) + t0 + jq, lg);
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * f;
+            }
             if (norm_here || stats_out) {
                 float sum = 0.f;
 #pragma unroll
@@ -942,6 +947,11 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const uint32_t rowi = (uint32_t)n * c.H + h;  // token-head row within the batch row
+    if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+        const float f = 1.f / decay_row_sum(row_pos0(c, b) + n, lg);
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * f;
+    }
     if (norm_here || stats_out) {
         float sum = 0.f;
 #pragma unroll

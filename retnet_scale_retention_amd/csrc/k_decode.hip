@@ -118,6 +118,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(MsrConst c, co
             out.w += p.w;
         }
     }
+    if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+        const float f = row_norm_factor(c, row_pos0(c, pair / c.H), c.log2g[h]);
+        out.x *= f;
+        out.y *= f;
+        out.z *= f;
+        out.w *= f;
+    }
     if (!(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const float s = owner ? (out.x + out.y + out.z + out.w) : 0.f;
         const float mean = block_sum(s, red) / c.dv;
@@ -265,6 +272,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(MsrConst c, const T
                 out.z += pv.z;
                 out.w += pv.w;
             }
+        }
+        if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+            const float f = row_norm_factor(c, p0 + t, c.log2g[h]);
+            out.x *= f;
+            out.y *= f;
+            out.z *= f;
+            out.w *= f;
         }
         if (!(c.flags & MSR_FLAG_NO_GROUPNORM)) {
             const float sm = owner ? (out.x + out.y + out.z + out.w) : 0.f;

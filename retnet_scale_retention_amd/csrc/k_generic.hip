@@ -145,6 +145,11 @@ __global__ __launch_bounds__(OUT_THREADS) void generic_output_kernel(
             }
         }
     }
+    if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+        const float f = row_norm_factor(c, row_pos0(c, b) + n, lg);
+#pragma unroll
+        for (int r = 0; r < OUT_COLS; ++r) acc[r] *= f;
+    }
     if (!(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         float s = 0.f;
 #pragma unroll

@@ -62,7 +62,7 @@ msr_status check_problem(const msr_problem *p, bool T1) {
         return fail(MSR_ERR_INVALID_ARG, "positions beyond 2^40 are not supported");
     if (p->pos_rows && (reinterpret_cast<uintptr_t>(p->pos_rows) & 7u))
         return fail(MSR_ERR_INVALID_ARG, "pos_rows is not 8-byte aligned");
-    if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM))
+    if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM | MSR_FLAG_DECAY_ROWNORM))
         return fail(MSR_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     return MSR_OK;
 }
@@ -319,6 +319,9 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; };
     const msr_problem pc = mfma_sub(p, dk, dv);
+    // the rows of O are the pre-norm outputs times a per-row factor when the
+    // decay is row-normalised: GroupNorm's input carries it, and so does G
+    const bool rownorm = p->flags & MSR_FLAG_DECAY_ROWNORM;
     // 1. Q~ and K~ (scaled) as two-term bf16 splits hi + lo.  The score
     //    products q~_n . k~_m go through hi.hi + lo.hi + hi.lo (retention is
     //    linear in its queries and in its keys): a score much smaller than
@@ -337,7 +340,12 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
         ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
         ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kl), V, P(b.oraw), nullptr, nullptr, P(b.mws), st));
         ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
+        if (rownorm) ok(launch_row_scale(c, dv, F(b.acc), MSR_F32, F(b.acc), MSR_F32, st));
         ok(launch_gn_backward(N, dv, c.eps, F(b.acc), MSR_F32, dO, BF, P(b.g), BF, st));
+        if (rownorm) ok(launch_row_scale(c, dv, P(b.g), BF, P(b.g), BF, st));
+        g = P(b.g);
+    } else if (rownorm) {
+        ok(launch_row_scale(c, dv, dO, BF, P(b.g), BF, st));
         g = P(b.g);
     }
     // 3. dq~ = sum over the d_v parts of Ret(G_part, V_part, K~; S_in^T rows of the part)
@@ -557,10 +565,13 @@ msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const voi
     pf.dtype = MSR_F32;
     pf.flags |= MSR_FLAG_NO_GROUPNORM;
     ok(generic_chunkwise(&pf, chunk, qf, kf, vf, oraw, state_in, nullptr, gws, st));
+    // (with row-normalised decay, oraw already carries the row factor, and G
+    // takes it once more: O = GN(f O_raw))
     if (!(p->flags & MSR_FLAG_NO_GROUPNORM))
         ok(launch_gn_backward(N, dv, c.eps, oraw, MSR_F32, dO, p->dtype, g, MSR_F32, st));
     else
         ok(launch_to_f32(p->dtype, N * dv, dO, g, st));
+    if (p->flags & MSR_FLAG_DECAY_ROWNORM) ok(launch_row_scale(c, dv, g, MSR_F32, g, MSR_F32, st));
     // 2. rotated (and scaled) Q~, K~, token-major fp32
     ok(launch_rotate_tok(c, qf, MSR_F32, qr, MSR_F32, 1.f, 1.f, st));
     ok(launch_rotate_tok(c, kf, MSR_F32, kr, MSR_F32, c.scale, 1.f, st));

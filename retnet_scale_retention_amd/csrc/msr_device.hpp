@@ -47,6 +47,21 @@ __device__ __forceinline__ void rot_cos_sin(int64_t pos, float theta, float &cs,
 // position of token 0 of batch row b
 __device__ __forceinline__ int64_t row_pos0(const MsrConst &c, int b) { return c.pos_rows ? c.pos_rows[b] : c.pos0; }
 
+// Sum of the decay weights of the row at absolute position p,
+// sum_{j=0}^{p} gamma^j = (1 - gamma^(p+1)) / (1 - gamma), formed as a ratio
+// of expm1 values so that gamma near 1 keeps its relative accuracy; p + 1
+// when gamma = 1.
+__device__ __forceinline__ float decay_row_sum(int64_t p, float log2g) {
+    if (log2g == 0.f) return (float)(p + 1);
+    const float l = log2g * 0.693147180559945f;
+    return expm1f((float)(p + 1) * l) / expm1f(l);
+}
+
+// 1 / decay_row_sum when the problem asks for row-normalised decay, else 1
+__device__ __forceinline__ float row_norm_factor(const MsrConst &c, int64_t p, float log2g) {
+    return (c.flags & MSR_FLAG_DECAY_ROWNORM) ? 1.f / decay_row_sum(p, log2g) : 1.f;
+}
+
 // gamma^d for d >= 0, as 2^(d * log2 gamma); never forms gamma^(-d).
 __device__ __forceinline__ float decay(float d, float log2g) { return exp2f(d * log2g); }
 

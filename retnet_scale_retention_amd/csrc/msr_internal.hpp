@@ -68,6 +68,9 @@ hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int
 hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int reverse, const void *x, int in_dtype,
                         void *y, int out_dtype, hipStream_t st);
 // y = x + (first ? 0 : y), y fp32
+// rows [B][T][H][d] times the row-normalised-decay factor of c at their positions
+hipError_t launch_row_scale(const MsrConst &c, int d, const void *x, int in_dtype, void *y, int out_dtype,
+                            hipStream_t st);
 hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, int first, hipStream_t st);
 // states [B][H][d1][d2] scaled by gamma_h^power (in NULL -> zeros); transpose != 0 writes
 // rows j0..j0+nj-1 of the transpose ([nj][d1] per pair)

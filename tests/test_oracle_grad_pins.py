@@ -5,7 +5,7 @@ torch float64, differentiated by autograd).
   implementation, for every option the backward pass takes.
 - Its gradients equal central finite differences of the C oracle's forward
   along random directions, for Q, K, V and the incoming state, with and
-  without GroupNorm and rotation.
+  without GroupNorm and rotation, and with the row-normalised decay.
 - With one token, no rotation and no GroupNorm the gradients have a closed
   form, checked directly.
 """
@@ -32,11 +32,13 @@ GAMMA = np.array([0.96875, 0.75], np.float32)
 @pytest.mark.parametrize("rotate", [True, False])
 @pytest.mark.parametrize("groupnorm", [True, False])
 @pytest.mark.parametrize("with_state", [True, False])
-def test_forward_matches_the_c_oracle(rotate, groupnorm, with_state):
+@pytest.mark.parametrize("rownorm", [False, True])
+def test_forward_matches_the_c_oracle(rotate, groupnorm, with_state, rownorm):
     q, k, v, s = inputs(1)
     s = s if with_state else None
-    ro, rs = orc.parallel(q, k, v, GAMMA, s_in=s, pos0=7, rotate=rotate, groupnorm=groupnorm)
-    o, so = og.forward(q, k, v, GAMMA, s_in=s, pos0=7, rotate=rotate, groupnorm=groupnorm)
+    kw = dict(s_in=s, pos0=7, rotate=rotate, groupnorm=groupnorm, rownorm=rownorm)
+    ro, rs = orc.parallel(q, k, v, GAMMA, **kw)
+    o, so = og.forward(q, k, v, GAMMA, **kw)
     assert rel(o, ro) < 1e-12 and rel(so, rs) < 1e-12
 
 
@@ -55,13 +57,15 @@ def loss_c(q, k, v, s, do, ds, **kw):
     return float(np.sum(o * do) + np.sum(so * ds))
 
 
-@pytest.mark.parametrize("rotate,groupnorm", [(True, True), (False, True), (True, False)])
-def test_gradients_match_finite_differences_of_the_c_oracle(rotate, groupnorm):
+@pytest.mark.parametrize("rotate,groupnorm,rownorm", [(True, True, False), (False, True, False),
+                                                      (True, False, False), (True, True, True),
+                                                      (True, False, True)])
+def test_gradients_match_finite_differences_of_the_c_oracle(rotate, groupnorm, rownorm):
     q, k, v, s = inputs(3)
     rng = np.random.default_rng(30)
     do = rng.standard_normal(q.shape[:3] + (v.shape[3],))
     ds = rng.standard_normal(s.shape)
-    kw = dict(pos0=5, rotate=rotate, groupnorm=groupnorm)
+    kw = dict(pos0=5, rotate=rotate, groupnorm=groupnorm, rownorm=rownorm)
     grads = og.backward(q, k, v, GAMMA, do, grad_state=ds, s_in=s, **kw)
     base = [q, k, v, s]
     for i, gr in enumerate(grads):

@@ -299,3 +299,62 @@ def test_parallel_rows_match_full_parallel():
     for h in range(2):
         r = orc.parallel_rows(q[0, :, h], k[0, :, h], v[0, :, h], g[h], rows, s_in=s[0, h], pos0=2)
         assert rel(r, o[0, rows, h]) < 1e-13
+
+
+# ------------------------------------------------- row-normalised decay (option)
+@pytest.mark.parametrize("form", ["parallel", "recurrent", "chunk4"])
+def test_row_normalised_decay_of_a_constant_sequence_is_one(form):
+    """Q = K = V = 1, no rotation, scale 1/d_k, no GroupNorm: every score is 1
+    and the raw output of the token at position p is the decay row sum
+    sum_{j<=p} gamma^j, so the row-normalised output is exactly 1.  The
+    second call continues the sequence at pos0 = 16 from the state the first
+    call left (the state stands for the earlier positions), and must also
+    give 1; counting only the call's own tokens would not."""
+    B, T, H, dk, dv = 1, 16, 2, 4, 6
+    g = np.array([0.9, 0.5], np.float32)
+    ones = lambda d: np.ones((B, T, H, d))
+    run = {"parallel": orc.parallel, "recurrent": orc.recurrent,
+           "chunk4": lambda *a, **kw: orc.chunkwise(*a[:4], 4, **kw)}[form]
+    kw = dict(rotate=False, groupnorm=False, scale=1.0 / dk, rownorm=True)
+    o1, s1 = run(ones(dk), ones(dk), ones(dv), g, **kw)
+    o2, _ = run(ones(dk), ones(dk), ones(dv), g, s_in=s1, pos0=T, **kw)
+    assert np.allclose(o1, 1.0, rtol=1e-13, atol=0) and np.allclose(o2, 1.0, rtol=1e-13, atol=0)
+    # closed form of the factor: the raw output times (1 - g)/(1 - g^(p+1))
+    raw, _ = run(ones(dk), ones(dk), ones(dv), g, s_in=s1, pos0=T, rotate=False, groupnorm=False, scale=1.0 / dk)
+    p = T + np.arange(T)
+    for h in range(H):
+        gh = np.float64(g[h])
+        assert np.allclose(raw[0, :, h, 0], (1 - gh ** (p + 1)) / (1 - gh), rtol=1e-13, atol=0)
+
+
+def test_row_normalised_decay_split_calls_equal_one_call():
+    """A sequence split over two calls (state carried, positions continued)
+    gives the same row-normalised outputs as one call."""
+    q, k, v, s = tiny(seed=14, T=48)
+    g = mi.gammas(2)
+    T1 = 20
+    kw = dict(rownorm=True, groupnorm=False)
+    o_all, _ = orc.parallel(q, k, v, g, s_in=s, pos0=3, **kw)
+    o1, s1 = orc.parallel(q[:, :T1], k[:, :T1], v[:, :T1], g, s_in=s, pos0=3, **kw)
+    o2, _ = orc.chunkwise(q[:, T1:], k[:, T1:], v[:, T1:], g, 4, s_in=s1, pos0=3 + T1, **kw)
+    assert rel(np.concatenate([o1, o2], 1), o_all) < 1e-12
+
+
+def test_row_normalised_decay_under_groupnorm_moves_only_eps():
+    """GroupNorm of x / r equals (x - mean) / sqrt(var + r^2 eps): with the
+    raw outputs x and the row sums r, the normalised-decay output is
+    GroupNorm with a per-row epsilon r^2 eps."""
+    q, k, v, s = tiny(seed=15, T=24)
+    g = np.array([0.9, 0.6], np.float32)
+    eps = 1e-2
+    raw, _ = orc.parallel(q, k, v, g, s_in=s, pos0=5, groupnorm=False)
+    o, _ = orc.parallel(q, k, v, g, s_in=s, pos0=5, eps=eps, rownorm=True)
+    p = 5 + np.arange(24)
+    for h in range(2):
+        gh = np.float64(g[h])
+        r = (1 - gh ** (p + 1)) / (1 - gh)
+        x = raw[0, :, h]
+        mean = x.mean(-1, keepdims=True)
+        var = ((x - mean) ** 2).mean(-1, keepdims=True)
+        expect = (x - mean) / np.sqrt(var + (r ** 2)[:, None] * np.float64(np.float32(eps)))
+        assert rel(o[0, :, h], expect) < 1e-12
