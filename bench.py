@@ -18,10 +18,14 @@ already resident in HBM.  The same JSON line also reports
   - parallel: the parallel form over the same 7B-shaped layer (O(T^2) score
     blocks, one call), algorithmic flops (T+1)(d_k+d_v) + 4 d_k d_v per token
     and head;
+  - backward: msr_chunkwise_backward on the small and the 7B-shaped layers;
+  - qkv: the Q/K/V projections (d_model = 4096) with the rotation in the
+    GEMM epilogue, and the projections + chunkwise form together;
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward] [--copy-mib N]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward]
+                  [--no-qkv] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -231,6 +235,47 @@ def bench_backward(torch, msr, mi, name, calls, chunk):
             "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms / 1e3), "tflops": flops / (ms / 1e3) / 1e12}
 
 
+def bench_qkv(torch, msr, mi, calls, chunk):
+    """The Q/K/V projections (bf16 MFMA GEMM with the rotation in its
+    epilogue) over the 7B-shaped layer input, d_model = H d_k = 4096, and the
+    composite projections + chunkwise form."""
+    w = mi.WORKLOADS["7b"]
+    dev = torch.device("cuda:0")
+    dm = w.H * w.dk
+    g = mi.gammas(w.H)
+    x = mi.device_normal((w.B, w.T, dm), 7001, dev, torch.bfloat16)
+    wts = [(mi.device_normal((w.H * d, dm), 7002 + i, dev, torch.float32) / np.sqrt(dm)).to(torch.bfloat16)
+           for i, d in enumerate((w.dk, w.dk, w.dv))]
+    out = (torch.empty((w.B, w.T, w.H, w.dk), dtype=torch.bfloat16, device=dev),
+           torch.empty((w.B, w.T, w.H, w.dk), dtype=torch.bfloat16, device=dev),
+           torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev))
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_QKV_CHUNKWISE,
+                                        chunk), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(calls):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / calls
+
+    ms_p = timed(lambda: msr.msr_qkv_projection(x, *wts, w.H, out=out))
+    ms_l = timed(lambda: msr.msr_qkv_chunkwise(x, *wts, g, chunk, out=o, state_out=s, workspace=ws))
+    flops = 2.0 * w.B * w.T * dm * w.H * (2 * w.dk + w.dv)
+    return {"config": {"workload": "7B-shaped layer input", "B": w.B, "T": w.T, "d_model": dm, "H": w.H,
+                       "dk": w.dk, "dv": w.dv, "chunk": chunk, "dtype": "bf16"},
+            "projection_ms": ms_p, "projection_tflops": flops / (ms_p / 1e3) / 1e12,
+            "projection_mfma_frac": flops / (ms_p / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "layer_ms": ms_l, "layer_tokens_per_s": w.B * w.T / (ms_l / 1e3)}
+
+
 def bench_decode(torch, msr, mi, nsteps):
     w = mi.WORKLOADS["decode"]
     dev = torch.device("cuda:0")
@@ -345,6 +390,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -373,6 +419,7 @@ def main():
     if not args.no_backward:
         bwd = {"small": bench_backward(torch, msr, mi, "small", 3, 64),
                "7b": bench_backward(torch, msr, mi, "7b", 5, 128)}
+    qkv = None if args.no_qkv else bench_qkv(torch, msr, mi, 5, args.chunk)
     cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
@@ -406,6 +453,7 @@ def main():
         "decode": dec,
         "parallel": par,
         "backward": bwd,
+        "qkv": qkv,
         "hbm_view": {"bytes_per_step": r["bytes"],
                      "achieved_GBs": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9,
                      "frac": r["bytes"] / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS},

@@ -97,7 +97,13 @@ typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
 enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u, MSR_FLAG_DECAY_ROWNORM = 4u };
 
 /* forms, for msr_workspace_size */
-enum { MSR_FORM_PARALLEL = 0, MSR_FORM_CHUNKWISE = 1, MSR_FORM_STEP = 2, MSR_FORM_BACKWARD = 3 };
+enum {
+    MSR_FORM_PARALLEL = 0,
+    MSR_FORM_CHUNKWISE = 1,
+    MSR_FORM_STEP = 2,
+    MSR_FORM_BACKWARD = 3,
+    MSR_FORM_QKV_CHUNKWISE = 4 /* msr_qkv_chunkwise */
+};
 
 typedef struct {
     int32_t B, T, H, dk, dv; /* dk even, 2..MSR_MAX_DK; dv 4..MSR_MAX_DV, multiple of 4 */
@@ -177,6 +183,40 @@ msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const voi
                                   const void *V, const float *state_in, const void *dO,
                                   const float *dstate_out, void *dQ, void *dK, void *dV, float *dstate_in,
                                   void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Q/K/V projections of the layer input, the step in front of retention
+ * (jsqmd.com section 2: the input goes through linear layers to give Q, K
+ * and V, then Q is rotated by Theta and K by its conjugate):
+ *   Q = R(X Wq^T),  K = s R(X Wk^T),  V = X Wv^T
+ * with the rotation R and the scale s (p->scale, 0 => dk^-0.5) of the forms,
+ * applied to the fp32 products before the one rounding to bf16.  With
+ * MSR_FLAG_NO_ROTATE in p->flags the plain products are written (no rotation,
+ * no scale).  Q, K so produced feed the forms with MSR_FLAG_NO_ROTATE and
+ * scale 1 (msr_qkv_chunkwise does exactly that).
+ *   X  [B][T][d_model] bf16; Wq, Wk [H*dk][d_model], Wv [H*dv][d_model] bf16
+ *      (a linear layer's weight layout: output features by input features);
+ *   Q, K [B][T][H][dk], V [B][T][H][dv] bf16, written.
+ * p->dtype must be MSR_BF16 (else MSR_ERR_UNSUPPORTED); d_model must be a
+ * positive multiple of 64 and H*dk a multiple of 4 (else MSR_ERR_SHAPE).
+ * p->gamma is not used.  Outputs must not overlap inputs or each other.
+ * Needs no workspace.
+ */
+msr_status msr_qkv_projection(const msr_problem *p, int32_t d_model, const void *X, const void *Wq,
+                              const void *Wk, const void *Wv, void *Q, void *K, void *V,
+                              void *hip_stream);
+
+/*
+ * The projections above followed by the chunkwise form: O and the outgoing
+ * state of msr_chunkwise(p, chunk, R(X Wq^T), X Wk^T, X Wv^T), the rotation
+ * and scale applied once, in the projection.  Q~, K~ and V live in the
+ * workspace: msr_workspace_size(p, MSR_FORM_QKV_CHUNKWISE, chunk) bytes.
+ * Same argument rules as msr_qkv_projection and msr_chunkwise.
+ */
+msr_status msr_qkv_chunkwise(const msr_problem *p, int32_t chunk, int32_t d_model, const void *X,
+                             const void *Wq, const void *Wk, const void *Wv, void *O,
+                             const float *state_in, float *state_out, void *ws, size_t ws_bytes,
+                             void *hip_stream);
 
 /*
  * One recurrent decode step for every pair, p->T must be 1 and p->pos0 is

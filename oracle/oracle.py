@@ -200,6 +200,13 @@ def rotate(x, *, theta=None, pos0=0, factor=1.0):
     return y
 
 
+def project(x, w):
+    """A linear layer without bias, x [..., d_model] times w [out, d_model]
+    transposed, in fp64: the projections that give Q, K and V from the
+    layer input (jsqmd.com s2)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
 def groupnorm(x, eps=1e-5):
     """GroupNorm over the last axis of x (one group per row), no affine."""
     x = _f64(x).copy()

@@ -392,6 +392,48 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     return e;
 }
 
+// ---- Q/K/V projections -------------------------------------------------
+
+// the chunkwise problem over projected inputs: rotation and scale already applied
+msr_problem qkv_sub(const msr_problem *p) {
+    msr_problem r = *p;
+    r.flags |= MSR_FLAG_NO_ROTATE;
+    r.scale = 1.f;
+    return r;
+}
+
+struct QkvPlan {
+    size_t q = 0, k = 0, v = 0, total = 0;
+};
+
+QkvPlan qkv_plan(const msr_problem *p) {
+    QkvPlan b;
+    const size_t M = (size_t)p->B * p->T;
+    b.q = 0;
+    b.k = round_up(M * p->H * p->dk * 2);
+    b.v = b.k + round_up(M * p->H * p->dk * 2);
+    b.total = b.v + round_up(M * p->H * p->dv * 2);
+    return b;
+}
+
+msr_status check_qkv(const msr_problem *p, int d_model, const void *X, const void *Wq, const void *Wk,
+                     const void *Wv) {
+    msr_status s = check_problem(p, false);
+    if (s != MSR_OK) return s;
+    if (p->dtype != MSR_BF16) return fail(MSR_ERR_UNSUPPORTED, "the projections take bf16 only");
+    if (d_model <= 0 || d_model % 64 != 0)
+        return fail(MSR_ERR_SHAPE, "d_model=%d must be a positive multiple of 64", d_model);
+    if ((p->H * p->dk) % 4 != 0) return fail(MSR_ERR_SHAPE, "H*dk=%d must be a multiple of 4", p->H * p->dk);
+    const bool any = (size_t)p->B * p->T > 0;
+    const void *in[4] = {X, Wq, Wk, Wv};
+    const char *names[4] = {"X", "Wq", "Wk", "Wv"};
+    for (int i = 0; i < 4; ++i) {
+        if (any && !in[i]) return fail(MSR_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (in[i] && !aligned16(in[i])) return fail(MSR_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    return MSR_OK;
+}
+
 }  // namespace
 
 void main_kernel_begin(hipStream_t st) {
@@ -426,6 +468,14 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
         if (p->dv > MSR_MAX_DK)
             return fail(MSR_ERR_UNSUPPORTED, "the backward pass needs dv <= %d (dv=%d)", MSR_MAX_DK, p->dv);
         *bytes = mfma_backward_ok(p, chunk) ? back_plan_mfma(p, chunk).total : back_plan(p, chunk).total;
+        return MSR_OK;
+    }
+    if (form == MSR_FORM_QKV_CHUNKWISE) {
+        if (chunk < 1) return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1", chunk);
+        const msr_problem sub = qkv_sub(p);
+        size_t inner = 0;
+        if ((s = msr_workspace_size(&sub, MSR_FORM_CHUNKWISE, chunk, &inner)) != MSR_OK) return s;
+        *bytes = qkv_plan(p).total + inner;
         return MSR_OK;
     }
     if (form == MSR_FORM_CHUNKWISE) {
@@ -509,6 +559,54 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     }
 
     return hip_status(generic_chunkwise(p, chunk, Q, K, V, O, state_in, state_out, ws, st), "generic chunkwise");
+}
+
+msr_status msr_qkv_projection(const msr_problem *p, int32_t d_model, const void *X, const void *Wq,
+                              const void *Wk, const void *Wv, void *Q, void *K, void *V, void *hip_stream) {
+    msr_status s = check_qkv(p, d_model, X, Wq, Wk, Wv);
+    if (s != MSR_OK) return s;
+    const size_t M = (size_t)p->B * p->T;
+    if (M == 0) return MSR_OK;
+    if (M > (size_t)INT32_MAX) return fail(MSR_ERR_SHAPE, "B*T is too large");
+    const void *outs[3] = {Q, K, V};
+    const char *on[3] = {"Q", "K", "V"};
+    const void *ins[4] = {X, Wq, Wk, Wv};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) return fail(MSR_ERR_INVALID_ARG, "%s is NULL", on[i]);
+        if (!aligned16(outs[i])) return fail(MSR_ERR_INVALID_ARG, "%s is not 16-byte aligned", on[i]);
+        for (int j = 0; j < 4; ++j)
+            if (outs[i] == ins[j]) return fail(MSR_ERR_INVALID_ARG, "%s must not alias an input", on[i]);
+        for (int j = 0; j < i; ++j)
+            if (outs[i] == outs[j]) return fail(MSR_ERR_INVALID_ARG, "%s must not alias %s", on[i], on[j]);
+    }
+    const MsrConst c = make_const(p, p->T);
+    const void *W[3] = {Wq, Wk, Wv};
+    void *Y[3] = {Q, K, V};
+    const int n[3] = {p->H * p->dk, p->H * p->dk, p->H * p->dv};
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    return hip_status(launch_proj(c, (int)M, d_model, X, W, Y, n, !(p->flags & MSR_FLAG_NO_ROTATE), st),
+                      "qkv projection");
+}
+
+msr_status msr_qkv_chunkwise(const msr_problem *p, int32_t chunk, int32_t d_model, const void *X,
+                             const void *Wq, const void *Wk, const void *Wv, void *O, const float *state_in,
+                             float *state_out, void *ws, size_t ws_bytes, void *hip_stream) {
+    msr_status s = check_qkv(p, d_model, X, Wq, Wk, Wv);
+    if (s != MSR_OK) return s;
+    size_t need = 0;
+    if ((s = msr_workspace_size(p, MSR_FORM_QKV_CHUNKWISE, chunk, &need)) != MSR_OK) return s;
+    if (!ws || ws_bytes < need)
+        return fail(MSR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+    if (!aligned16(ws)) return fail(MSR_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    const QkvPlan b = qkv_plan(p);
+    char *w = static_cast<char *>(ws);
+    const msr_problem sub = qkv_sub(p);
+    // validate the retention call before anything runs
+    if ((s = check_tensors(&sub, w + b.q, w + b.k, w + b.v, O, state_in, state_out)) != MSR_OK) return s;
+    if ((s = msr_qkv_projection(p, d_model, X, Wq, Wk, Wv, w + b.q, w + b.k, w + b.v, hip_stream)) != MSR_OK)
+        return s;
+    return msr_chunkwise(&sub, chunk, w + b.q, w + b.k, w + b.v, O, state_in, state_out, w + b.total,
+                         ws_bytes - b.total, hip_stream);
 }
 
 msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const void *Q, const void *K,

@@ -68,6 +68,11 @@ hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int
 hipError_t launch_slice(int B, int T, int H, int d, int col0, int len, int reverse, const void *x, int in_dtype,
                         void *y, int out_dtype, hipStream_t st);
 // y = x + (first ? 0 : y), y fp32
+// Q/K/V projections (k_proj.hip): Y[i] = X W[i]^T for the three matrices, X
+// [M][d_model], W[i] [n[i]][d_model], Y[i] [M][n[i]], all bf16; with rotate,
+// Y[0] and Y[1] rotated at each token's position and Y[1] scaled by c.scale
+hipError_t launch_proj(const MsrConst &c, int M, int d_model, const void *X, const void *const W[3],
+                       void *const Y[3], const int n[3], int rotate, hipStream_t st);
 // rows [B][T][H][d] times the row-normalised-decay factor of c at their positions
 hipError_t launch_row_scale(const MsrConst &c, int d, const void *x, int in_dtype, void *y, int out_dtype,
                             hipStream_t st);

@@ -19,12 +19,13 @@ LIB_PATH = Path(os.environ.get("MSR_LIB", Path(__file__).resolve().parent / "lib
 MSR_OK = 0
 MSR_F32, MSR_BF16 = 0, 1
 MSR_FLAG_NO_ROTATE, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_DECAY_ROWNORM = 1, 2, 4
-MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD = 0, 1, 2, 3
+MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD, MSR_FORM_QKV_CHUNKWISE = 0, 1, 2, 3, 4
 STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_ERR_DTYPE",
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
 EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_parallel",
-           "msr_chunkwise", "msr_chunkwise_backward", "msr_recurrent_step", "msr_set_kernel_events")
+           "msr_chunkwise", "msr_chunkwise_backward", "msr_qkv_projection", "msr_qkv_chunkwise",
+           "msr_recurrent_step", "msr_set_kernel_events")
 
 
 class MsrError(RuntimeError):
@@ -69,6 +70,11 @@ def load():
     lib.msr_chunkwise_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_size_t, vp]
     lib.msr_chunkwise_backward.restype = ctypes.c_int
+    lib.msr_qkv_projection.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msr_qkv_projection.restype = ctypes.c_int
+    lib.msr_qkv_chunkwise.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+    lib.msr_qkv_chunkwise.restype = ctypes.c_int
     lib.msr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.msr_recurrent_step.restype = ctypes.c_int
     lib.msr_set_kernel_events.argtypes = [vp, vp]
@@ -231,6 +237,59 @@ def msr_chunkwise_backward(q, k, v, gamma, chunk, grad_out, *, grad_state=None, 
                                          _ptr(ds), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                                          _stream(q, stream)))
     return dq, dk_, dv_, ds
+
+
+def _qkv_args(x, wq, wk, wv, H):
+    for name, t in (("x", x), ("wq", wq), ("wk", wk), ("wv", wv)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if x.dim() != 3 or wq.dim() != 2 or wk.shape != wq.shape or wv.dim() != 2:
+        raise ValueError("expected x [B, T, d_model], wq, wk [H dk, d_model], wv [H dv, d_model]")
+    B, T, dm = x.shape
+    if wq.shape[1] != dm or wv.shape[1] != dm or wq.shape[0] % H or wv.shape[0] % H:
+        raise ValueError("weight shapes do not match d_model and H")
+    return B, T, dm, wq.shape[0] // H, wv.shape[0] // H
+
+
+def msr_qkv_projection(x, wq, wk, wv, H, *, theta=None, scale=0.0, pos0=0, flags=0, pos_rows=None,
+                       out=None, stream=None):
+    """Q = R(x wq^T), K = s R(x wk^T), V = x wv^T as [B, T, H, d] bf16
+    (x [B, T, d_model] bf16, weights [H d, d_model]).  Returns (Q, K, V)."""
+    torch = _torch()
+    B, T, dm, dk, dv = _qkv_args(x, wq, wk, wv, H)
+    d = _Desc(B, T, H, dk, dv, _dtype_code(x), np.ones(H, np.float32), theta, scale, 1e-5, pos0, flags,
+              _pos_rows(pos_rows, B, x.device))
+    if out is None:
+        out = (torch.empty((B, T, H, dk), dtype=x.dtype, device=x.device),
+               torch.empty((B, T, H, dk), dtype=x.dtype, device=x.device),
+               torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device))
+    _check(load().msr_qkv_projection(d.ref, int(dm), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv),
+                                     *(_ptr(t) for t in out), _stream(x, stream)))
+    return out
+
+
+def msr_qkv_chunkwise(x, wq, wk, wv, gamma, chunk, *, theta=None, scale=0.0, eps=1e-5, pos0=0, flags=0,
+                      state_in=None, return_state=True, out=None, state_out=None, workspace=None,
+                      stream=None, pos_rows=None):
+    """The projections followed by the chunkwise form: returns (O, state_out
+    or None) for the layer input x [B, T, d_model] and weights [H d, d_model]."""
+    torch = _torch()
+    H = len(np.atleast_1d(gamma))
+    B, T, dm, dk, dv = _qkv_args(x, wq, wk, wv, H)
+    d = _Desc(B, T, H, dk, dv, _dtype_code(x), gamma, theta, scale, eps, pos0, flags,
+              _pos_rows(pos_rows, B, x.device))
+    n = ctypes.c_size_t(0)
+    _check(load().msr_workspace_size(d.ref, MSR_FORM_QKV_CHUNKWISE, chunk, ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=x.device)
+    _check(load().msr_qkv_chunkwise(d.ref, int(chunk), int(dm), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv),
+                                    _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(workspace),
+                                    ctypes.c_size_t(workspace.numel()), _stream(x, stream)))
+    return out, state_out
 
 
 def msr_recurrent_step(q, k, v, state, gamma, pos, *, theta=None, scale=0.0, eps=1e-5, flags=0,

@@ -358,3 +358,18 @@ def test_row_normalised_decay_under_groupnorm_moves_only_eps():
         var = ((x - mean) ** 2).mean(-1, keepdims=True)
         expect = (x - mean) / np.sqrt(var + (r ** 2)[:, None] * np.float64(np.float32(eps)))
         assert rel(o[0, :, h], expect) < 1e-12
+
+
+# ------------------------------------------------------ Q/K/V projections
+def test_projection_brute_force_and_identity():
+    """The projection is the plain sum y[t][o] = sum_i x[t][i] w[o][i]:
+    checked against explicit loops, and identity weights return x."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((2, 3, 5))
+    w = rng.standard_normal((4, 5))
+    y = orc.project(x, w)
+    for b in range(2):
+        for t in range(3):
+            for o in range(4):
+                assert abs(y[b, t, o] - sum(x[b, t, i] * w[o, i] for i in range(5))) < 1e-13
+    assert np.array_equal(orc.project(x, np.eye(5)), x)
