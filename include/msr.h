@@ -65,7 +65,8 @@
 extern "C" {
 #endif
 
-#define MSR_ABI_VERSION 2
+/* 3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection, msr_qkv_chunkwise (2: pos_rows) */
+#define MSR_ABI_VERSION 3
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
 #define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
 #define MSR_MAX_DV 1024   /* d_v limit */

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msr_abi_version() == 2
+    assert lib.msr_abi_version() == 3
 
 
 def test_problem_struct_layout_matches_the_header():
@@ -123,6 +123,32 @@ def test_calls_validate_pointers_before_any_launch():
                                O, O, null)
     assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
     assert "alias" in lib.msr_last_error().decode()
+
+
+def test_qkv_calls_validate_before_any_launch():
+    lib = msr.load()
+    null = ctypes.c_void_p()
+    outs = [ctypes.c_void_p(0x50000 + 0x10000 * i) for i in range(3)]
+    # fp32 is not taken
+    s = lib.msr_qkv_projection(desc(dtype=m.MSR_F32).ref, 64, FAKE, FAKE, FAKE, FAKE, *outs, null)
+    assert m.STATUS[s] == "MSR_ERR_UNSUPPORTED"
+    # d_model must be a positive multiple of 64
+    for dm in (0, 48, 100):
+        s = lib.msr_qkv_projection(desc().ref, dm, FAKE, FAKE, FAKE, FAKE, *outs, null)
+        assert m.STATUS[s] == "MSR_ERR_SHAPE"
+    # missing or misaligned input, output aliasing an input
+    s = lib.msr_qkv_projection(desc().ref, 64, null, FAKE, FAKE, FAKE, *outs, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    s = lib.msr_qkv_projection(desc().ref, 64, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, *outs, null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG"
+    s = lib.msr_qkv_projection(desc().ref, 64, FAKE, FAKE, FAKE, FAKE, FAKE, outs[1], outs[2], null)
+    assert m.STATUS[s] == "MSR_ERR_INVALID_ARG" and "alias" in lib.msr_last_error().decode()
+    # the composite needs its workspace: Q~, K~, V plus the chunkwise form's
+    s, n = status_ws(desc(), m.MSR_FORM_QKV_CHUNKWISE, 16)
+    s1, n1 = status_ws(desc(), m.MSR_FORM_CHUNKWISE, 16)
+    assert s == 0 and s1 == 0 and n >= n1 + 2 * 64 * 4 * (2 * 16 + 32)
+    s = lib.msr_qkv_chunkwise(desc().ref, 16, 64, FAKE, FAKE, FAKE, FAKE, outs[0], null, null, FAKE, 16, null)
+    assert m.STATUS[s] == "MSR_ERR_WORKSPACE"
 
 
 def test_null_problem_and_bytes():
