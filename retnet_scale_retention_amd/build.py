@@ -26,7 +26,7 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang"
 # which serialises the matrix pipe (a 16x16x32 bf16 MFMA loop with one wave
 # per SIMD then issues every ~31 clocks instead of ~19)
 MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-MFMA_SOURCES = {"k_chunk_mfma.hip"}
+MFMA_SOURCES = {"k_chunk_mfma.hip", "k_proj.hip"}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{ROOT / 'include'}", f"-I{CSRC}"]
 
