@@ -243,11 +243,18 @@ struct ChunkArgs {
 // Q~ layout (kq, the A operand of the parallel kernel's score products), and
 // the KF fragments carry s gamma^(T-1-t) for the state sum
 // S_out = gamma^T S_in + sum_t gamma^(T-1-t) k~_t^T v_t.
-template <int DK, int BC, bool PAR>
+//
+// SPLIT: q and k come with low parts qlo, klo of the same layout (two-term
+// bf16 splits of more precise operands); the scores then take
+// hi.hi + lo.hi + hi.lo, the lo fragments read straight from global memory.
+// Everything else uses the hi parts.
+template <int DK, int BC, bool PAR, bool SPLIT = false>
 __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
                                                                   const uint16_t *__restrict__ k,
                                                                   uint16_t *__restrict__ qf, uint16_t *__restrict__ kf,
-                                                                  uint16_t *__restrict__ pf, uint16_t *__restrict__ kq) {
+                                                                  uint16_t *__restrict__ pf, uint16_t *__restrict__ kq,
+                                                                  const uint16_t *__restrict__ qlo = nullptr,
+                                                                  const uint16_t *__restrict__ klo = nullptr) {
     using C = Cfg<DK, BC>;
     constexpr int NT = C::PREP_NT, PW = NT / 64;  // threads, waves
     constexpr int C8 = DK / 8;                    // 16-byte channel groups per row
@@ -405,6 +412,28 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
 #pragma unroll
                     for (int v2 = 0; v2 < 2; ++v2) acc[u][v2] = mfma16(ka[v2], qb[u], acc[u][v2]);
                 }
+            if constexpr (SPLIT) {
+                const char *ql = reinterpret_cast<const char *>(qlo + base);
+                const char *kl = reinterpret_cast<const char *>(klo + base);
+                bf16x8 kla[2], qlb[NU];
+#pragma unroll
+                for (int v2 = 0; v2 < 2; ++v2)
+                    kla[v2] = __builtin_bit_cast(bf16x8, ld16(kl, (uint32_t)(32 * kb + 16 * v2 + l16) * rowQK +
+                                                                      (32 * ks + 8 * g) * 2));
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+                    qlb[u] = __builtin_bit_cast(bf16x8, ld16(ql, (uint32_t)(16 * qt[u] + l16) * rowQK +
+                                                                 (32 * ks + 8 * g) * 2));
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+                    if (nd[u]) {
+#pragma unroll
+                        for (int v2 = 0; v2 < 2; ++v2) {
+                            acc[u][v2] = mfma16(kla[v2], qb[u], acc[u][v2]);
+                            acc[u][v2] = mfma16(ka[v2], qlb[u], acc[u][v2]);
+                        }
+                    }
+            }
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -1029,13 +1058,23 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, co
 }
 
 template <int DK, int BC>
-hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, hipStream_t st) {
+hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, const void *Qlo,
+                        const void *Klo, hipStream_t st) {
     const int npairs = c.B * c.H;
-    auto pk = prep_kernel<DK, BC, false>;
     using C = Cfg<DK, BC>;
-    hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
-                       static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
-                       const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr);
+    if (Qlo && Klo) {
+        auto pk = prep_kernel<DK, BC, false, true>;
+        hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c,
+                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
+                           const_cast<uint16_t *>(a.qf), const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf),
+                           (uint16_t *)nullptr, static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo));
+    } else {
+        auto pk = prep_kernel<DK, BC, false>;
+        hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c,
+                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
+                           const_cast<uint16_t *>(a.qf), const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf),
+                           (uint16_t *)nullptr, (const uint16_t *)nullptr, (const uint16_t *)nullptr);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = npairs * a.nseg * a.NS;
@@ -1054,11 +1093,11 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, co
 
 template <int DK>
 hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, const void *Q, const void *K,
-                       hipStream_t st) {
+                       const void *Qlo, const void *Klo, hipStream_t st) {
     switch (chunk) {
-    case 64: return launch_chunk<DK, 64>(c, a, Q, K, st);
-    case 128: return launch_chunk<DK, 128>(c, a, Q, K, st);
-    case 256: return launch_chunk<DK, 256>(c, a, Q, K, st);
+    case 64: return launch_chunk<DK, 64>(c, a, Q, K, Qlo, Klo, st);
+    case 128: return launch_chunk<DK, 128>(c, a, Q, K, Qlo, Klo, st);
+    case 256: return launch_chunk<DK, 256>(c, a, Q, K, Qlo, Klo, st);
     default: return hipErrorNotSupported;
     }
 }
@@ -1123,7 +1162,8 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     float2 *stats = NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
     auto pk = prep_kernel<DK, 64, true>;
     hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
-                       static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq);
+                       static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq, (const uint16_t *)nullptr,
+                       (const uint16_t *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NS};
@@ -1189,7 +1229,7 @@ size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk) {
 
 hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, const void *Q,
                           const void *K, const void *V, void *O, const float *s_in, float *s_out,
-                          void *ws, hipStream_t st) {
+                          void *ws, hipStream_t st, const void *Qlo, const void *Klo) {
     const MfmaPlan m = mfma_plan(p, chunk);
     char *wsb = static_cast<char *>(ws);
     ChunkArgs a{};  // every field starts at zero (par = 0: chunkwise form)
@@ -1208,9 +1248,9 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
 
     hipError_t e = hipSuccess;
     switch (p->dk) {
-    case 64: e = dispatch_bc<64>(c, a, chunk, Q, K, st); break;
-    case 128: e = dispatch_bc<128>(c, a, chunk, Q, K, st); break;
-    case 256: e = dispatch_bc<256>(c, a, chunk, Q, K, st); break;
+    case 64: e = dispatch_bc<64>(c, a, chunk, Q, K, Qlo, Klo, st); break;
+    case 128: e = dispatch_bc<128>(c, a, chunk, Q, K, Qlo, Klo, st); break;
+    case 256: e = dispatch_bc<256>(c, a, chunk, Q, K, Qlo, Klo, st); break;
     default: e = hipErrorNotSupported;
     }
     if (e != hipSuccess) return e;

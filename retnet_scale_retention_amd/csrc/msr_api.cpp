@@ -276,7 +276,7 @@ BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
     b.p1 = take(N * 256 * 2);
     b.p2 = take(N * 256 * 2);
     b.part = take(N * dk * 2);
-    b.acc = take(N * (dk > dv ? dk : dv) * 4);
+    b.acc = take(N * dk * 4);
     b.tmp = take(N * dk * 4);
     const size_t sp = (size_t)p->B * p->H * 256 * dk * 4, sf = (size_t)p->B * p->H * dk * dv * 4;
     b.s1 = take(sp);
@@ -297,10 +297,12 @@ BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
 }
 
 // One retention call on the MFMA path (no rotation, no GroupNorm, scale 1).
+// (Qlo, Klo: low parts of two-term bf16 splits of Q and K for the scores)
 hipError_t mfma_ret(const msr_problem *sub, int chunk, const void *Q, const void *K, const void *V, void *O,
-                    const float *s_in, float *s_out, void *ws, hipStream_t st) {
+                    const float *s_in, float *s_out, void *ws, hipStream_t st, const void *Qlo = nullptr,
+                    const void *Klo = nullptr) {
     const MsrConst c = make_const(sub, chunk);
-    return mfma_chunkwise(c, sub, chunk, Q, K, V, O, s_in, s_out, ws, st);
+    return mfma_chunkwise(c, sub, chunk, Q, K, V, O, s_in, s_out, ws, st, Qlo, Klo);
 }
 
 hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const void *K, const void *V,
@@ -322,26 +324,21 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     // the rows of O are the pre-norm outputs times a per-row factor when the
     // decay is row-normalised: GroupNorm's input carries it, and so does G
     const bool rownorm = p->flags & MSR_FLAG_DECAY_ROWNORM;
-    // 1. Q~ and K~ (scaled) as two-term bf16 splits hi + lo.  The score
-    //    products q~_n . k~_m go through hi.hi + lo.hi + hi.lo (retention is
-    //    linear in its queries and in its keys): a score much smaller than
-    //    |q~||k~| loses its relative accuracy when q~ and k~ are rounded to
-    //    bf16, and GroupNorm's backward amplifies that error on rows built
-    //    from few tokens.  Elsewhere Q~ and K~ enter as hi.
+    // 1. Q~ and K~ (scaled) as two-term bf16 splits hi + lo.  The
+    //    intra-chunk score products q~_n . k~_m take hi.hi + lo.hi + hi.lo
+    //    (in prep_kernel): a score much smaller than |q~||k~| loses its
+    //    relative accuracy when q~ and k~ are rounded to bf16, and GroupNorm's
+    //    backward amplifies that error on rows built from few tokens.
+    //    Elsewhere Q~ and K~ enter as hi.
     ok(launch_rotate_tok(c, Q, BF, P(b.qr), BF, 1.f, 1.f, st, P(b.ql)));
     ok(launch_rotate_tok(c, K, BF, P(b.kr), BF, c.scale, 1.f, st, P(b.kl)));
-    // 2. outputs before GroupNorm in fp32 (three calls summed), then
-    //    G = dL/dO_raw (bf16) by GroupNorm's backward
+    // 2. outputs before GroupNorm (bf16), then G = dL/dO_raw (bf16) by
+    //    GroupNorm's backward
     const void *g = dO;
     if (!(p->flags & MSR_FLAG_NO_GROUPNORM)) {
-        ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kr), V, P(b.oraw), state_in, nullptr, P(b.mws), st));
-        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 1, st));
-        ok(mfma_ret(&pc, chunk, P(b.ql), P(b.kr), V, P(b.oraw), state_in, nullptr, P(b.mws), st));
-        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
-        ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kl), V, P(b.oraw), nullptr, nullptr, P(b.mws), st));
-        ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
-        if (rownorm) ok(launch_row_scale(c, dv, F(b.acc), MSR_F32, F(b.acc), MSR_F32, st));
-        ok(launch_gn_backward(N, dv, c.eps, F(b.acc), MSR_F32, dO, BF, P(b.g), BF, st));
+        ok(mfma_ret(&pc, chunk, P(b.qr), P(b.kr), V, P(b.oraw), state_in, nullptr, P(b.mws), st, P(b.ql), P(b.kl)));
+        if (rownorm) ok(launch_row_scale(c, dv, P(b.oraw), BF, P(b.oraw), BF, st));
+        ok(launch_gn_backward(N, dv, c.eps, P(b.oraw), BF, dO, BF, P(b.g), BF, st));
         if (rownorm) ok(launch_row_scale(c, dv, P(b.g), BF, P(b.g), BF, st));
         g = P(b.g);
     } else if (rownorm) {
@@ -373,21 +370,16 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     ok(launch_slice(B, T, H, dk, 0, dk, 1, F(b.acc), MSR_F32, F(b.tmp), MSR_F32, st));
     ok(launch_rotate_tok(c, F(b.tmp), MSR_F32, dK, BF, c.scale, -1.f, st));
     // 5. dV (backward in time) = Ret(K~, Q~, G; dS_out / gamma), its scores
-    //    split as in 1. (summed in fp32); the first call's outgoing state
-    //    times gamma is dS_in
+    //    split as in 1.; its outgoing state times gamma is dS_in
     ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kr), BF, P(b.krrev), BF, st));
     ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kl), BF, P(b.klrev), BF, st));
     ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.ql), BF, P(b.qlrev), BF, st));
     ok(launch_slice(B, T, H, dv, 0, dv, 1, g, BF, P(b.grev), BF, st));
     float *dso = dstate_out ? F(b.s3) : nullptr, *sc = dstate_in ? F(b.s4) : nullptr;
     if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, 0, dv, st));
-    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, sc, P(b.mws), st));
-    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 1, st));
-    ok(mfma_ret(&pc, chunk, P(b.klrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, nullptr, P(b.mws), st));
-    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
-    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qlrev), P(b.grev), P(b.oraw), nullptr, nullptr, P(b.mws), st));
-    ok(launch_accumulate(N * dv, P(b.oraw), BF, F(b.acc), 0, st));
-    ok(launch_slice(B, T, H, dv, 0, dv, 1, F(b.acc), MSR_F32, dV, BF, st));
+    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, sc, P(b.mws), st, P(b.klrev),
+                P(b.qlrev)));
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, P(b.oraw), BF, dV, BF, st));
     if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, 0, dv, st));
     return e;
 }
