@@ -20,7 +20,8 @@
 //   QF[pair][chunk][u][ks]  Q~, query rows 16 u.., d_k columns 32 ks..
 //                           (B operand of the inter-chunk product)
 //   KF[pair][chunk][rt][kb] (K~ zeta s)^T, d_k rows 16 rt.., tokens 32 kb..
-//                           with zeta_t s = s gamma^(b-1-t) and the rescale
+//                           in the key order of PF below, with
+//                           zeta_t s = s gamma^(b-1-t) and the rescale
 //                           factor gamma^(-b j) of the chunk applied
 //                           (A operand of the state update)
 //   PF[pair][chunk][u][kb]  P^T, keys 32 kb.., query columns 16 u.., keys in
@@ -360,17 +361,19 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     }
 
     // ---- (K~ zeta s)^T fragments: lane (n, g) of fragment (rt, kb) holds
-    // K~[t][16 rt + n] s gamma^(BC-1-t) gamma^(-BC j) for t = 32 kb + 8 g + e
+    // K~[t][16 rt + n] s gamma^(BC-1-t) gamma^(-BC j) for t = 32 kb + 4 g + e
+    // and t = 32 kb + 16 + 4 g + e (e = 0..3): the key order of the P^T
+    // fragments, so that one transposed read of V serves both products
     uint16_t *kfo = kf + (size_t)blockIdx.x * (C::RT * C::NB * FRAG) + lane * 8;
     for (int f = w; f < C::RT * C::NB; f += PW) {
         const int rt = f / C::NB, kb = f % C::NB;
-        const int row = 32 * kb + 8 * g + (l16 >> 2), col = 16 * rt + 4 * (l16 & 3);
-        const s16x4 lo = lds_tr(Ks + C::koff(row, col)), hi = lds_tr(Ks + C::koff(row + 4, col));
+        const int row = 32 * kb + 4 * g + (l16 >> 2), col = 16 * rt + 4 * (l16 & 3);
+        const s16x4 lo = lds_tr(Ks + C::koff(row, col)), hi = lds_tr(Ks + C::koff(row + 16, col));
         bf16x8 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = static_cast<__bf16>(bf(lo[e]) * zet[32 * kb + 8 * g + e]);
-            x[4 + e] = static_cast<__bf16>(bf(hi[e]) * zet[32 * kb + 8 * g + 4 + e]);
+            x[e] = static_cast<__bf16>(bf(lo[e]) * zet[32 * kb + 4 * g + e]);
+            x[4 + e] = static_cast<__bf16>(bf(hi[e]) * zet[32 * kb + 16 + 4 * g + e]);
         }
         *reinterpret_cast<bf16x8 *>(kfo + (size_t)f * FRAG) = x;
     }
@@ -731,13 +734,32 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             // the block R ahead (in this chunk or the next) reuses this slot
             const int nb = kb + C::R;
             const int ci2 = ci + nb / C::NB, kb2 = nb % C::NB;
+            // V of this block read transposed, keys in the order
+            // {4g..4g+3, 16+4g..16+4g+3} of lane group g -- the order of the
+            // P^T and (K~ zeta s)^T fragments.  When a wave's state tiles span
+            // all value columns (CG == 1) one read serves both products.
+            constexpr bool SHARE = !SO && C::CG == 1;
+            constexpr int NVA = C::CT;
+            s16x4 va[NVA][2];
+            if constexpr (!SO) {
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) {
+                    const int col = ct * 16 + 4 * (l16 & 3);
+                    va[ct][0] = lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col));
+                    va[ct][1] = lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col));
+                }
+            }
             {  // S += (K~ zeta s)^T V
-                const int tb = 32 * kb + 8 * g;
                 bf16x8 bv[C::CPW];
 #pragma unroll
                 for (int ct = 0; ct < C::CPW; ++ct) {
-                    const int col = (cbase + ct) * 16 + 4 * (l16 & 3);
-                    bv[ct] = cat(lds_tr(Vc + C::voff(tb + (l16 >> 2), col)), lds_tr(Vc + C::voff(tb + 4 + (l16 >> 2), col)));
+                    if constexpr (SHARE) {
+                        bv[ct] = cat(va[ct][0], va[ct][1]);
+                    } else {
+                        const int col = (cbase + ct) * 16 + 4 * (l16 & 3);
+                        bv[ct] = cat(lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col)),
+                                     lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col)));
+                    }
                 }
 #pragma unroll
                 for (int rt = 0; rt < C::RPW; ++rt)
@@ -748,13 +770,6 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             load_kp_k(ci2, kb2);
             vmem_fence();
             if (!SO) {  // O^T += V^T P^T for the query tiles that reach this block
-                s16x4 va[C::CT][2];
-#pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) {
-                    const int col = ct * 16 + 4 * (l16 & 3);
-                    va[ct][0] = lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col));
-                    va[ct][1] = lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col));
-                }
 #pragma unroll
                 for (int u = 0; u < C::NQT; ++u) {
                     if (!(32 * kb <= 16 * qt[u] + 15)) continue;
