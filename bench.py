@@ -97,6 +97,7 @@ def chunk_bytes(T, H, B, dk, dv):
 # device headers and the build script (whose flags shape the generated code).
 KERNEL_SOURCES = {
     "chunk_mfma_kernel": "k_chunk_mfma.hip",
+    "chunk_ws_kernel": "k_chunk_mfma.hip",
     "prep_kernel": "k_chunk_mfma.hip",
     "gn_finalize_kernel": "k_chunk_mfma.hip",
     "decode_kernel": "k_decode.hip",
@@ -428,7 +429,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    traffic = traffic_record("chunk_mfma_kernel")
+    # the chunk recurrence runs as the warp-specialised kernel for b <= 128
+    main_kernel = "chunk_ws_kernel" if args.chunk <= 128 else "chunk_mfma_kernel"
+    traffic = traffic_record(main_kernel)
     line = {
         "metric": "chunkwise MSR fwd tokens/s + decode steps/s; % of bf16 MFMA / HBM peak",
         "value": r["tokens_per_s"],
@@ -446,7 +449,7 @@ def main():
                    "dk": w.dk, "dv": w.dv, "chunk": r["chunk"], "state": "fp32"},
         "roofline": {"bound": "mfma", "achieved": r["kernel_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": r["kernel_tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic, "kernel": "chunk_mfma_kernel",
+                     "traffic": traffic, "kernel": main_kernel,
                      "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["kernel_flops"]},
         "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
         "cpu_baseline": cpu,

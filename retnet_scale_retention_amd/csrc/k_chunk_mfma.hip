@@ -622,6 +622,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     }
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+    const int64_t rp0 = (!SO && (c.flags & MSR_FLAG_DECAY_ROWNORM)) ? row_pos0(c, b) : 0;
     auto flush_u = [&](int u) {
         uint16_t *dst = obase + pend_row[u] * (uint32_t)c.dv;
 #pragma unroll
@@ -793,7 +794,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             const int jq = 16 * qt[u] + l16;
             pend_row[u] = (uint32_t)(t0 + jq) * c.H + h;
             if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
-                const float f = 1.f / decay_row_sum(row_pos0(c, b) + t0 + jq, lg);
+                const float f = 1.f / decay_row_sum(rp0 + t0 + jq, lg);
 #pragma unroll
                 for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * f;
             }
@@ -867,6 +868,346 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 }
     }
     // the clamped loads of the last chunk may still be in flight
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Warp-specialised variant of the full pass (b <= 128): 8 waves, two per
+// SIMD.  The four "O" waves (w < 4) run the inter-chunk product, the value
+// product and GroupNorm with the fragments of chunk kernel wave w; the four
+// "S" waves run the state update and the V loads with the state tiles of
+// wave w - 4.  Both kinds meet at one barrier per chunk; the S waves write
+// S_new^T for the next chunk's inter-chunk product into the other LDS
+// buffer.  The kernel is bound by the vector-memory requests each CU can
+// keep in flight (the fragments of a pair are read by all of its value
+// slices), so:
+//   - each fragment load is issued right after the last use of its
+//     registers, a chunk ahead of its next use (full scheduling barriers
+//     keep the compiler from sinking the loads to the end of the chunk);
+//   - V goes through registers (plain loads, stored to LDS at the end of the
+//     chunk), so no direct-to-LDS load is outstanding when the compiler
+//     waits for a fragment;
+//   - P^T fragments of key blocks a query tile does not reach are not loaded.
+template <int DK, int BC>
+__global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(MsrConst c, ChunkArgs a) {
+    using C = Cfg<DK, BC>;
+    static_assert(C::NW == 4 && C::QSTAGE, "warp-specialised pass: 4 + 4 waves, Q~ fragments carry xi");
+    __shared__ __attribute__((aligned(16))) char Vb0[C::VTILE], Vb1[C::VTILE];
+    __shared__ __attribute__((aligned(16))) __bf16 St0[W * C::SP], St1[W * C::SP];  // S_old^T
+
+    const int tid = threadIdx.x, lane = tid & 63, w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool srole = w8 >= C::NW;
+    const int w = srole ? w8 - C::NW : w8;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int npairs = c.B * c.H;
+    int pair, seg, slice;
+    {
+        const int id = blockIdx.x, nps = npairs * a.nseg;
+        int ps;
+        if (nps % 8 == 0) {
+            const int xcd = id & 7, j = id >> 3;
+            ps = (j / a.NS) * 8 + xcd;
+            slice = j % a.NS;
+        } else {
+            ps = id / a.NS;
+            slice = id % a.NS;
+        }
+        pair = ps / a.nseg;
+        seg = ps % a.nseg;
+    }
+    const int i0 = seg * a.seglen, i1 = i0 + a.seglen;
+    const int b = pair / c.H, h = pair % c.H;
+    const int col0 = slice * W;
+    const float lg = c.log2g[h];
+    const int period = rescale_period(lg, BC);
+    int ph = i0 == 0 ? 0 : (i0 - 1) % period;
+    const int nch = c.T / BC;
+    const size_t pc0 = (size_t)pair * nch;
+    const uint16_t *qfb = a.qf + pc0 * (C::NKT * C::KS * FRAG);
+    const uint16_t *kfb = a.kf + pc0 * (C::RT * C::NB * FRAG);
+    const uint16_t *pfb = a.pf + pc0 * (C::NKT * C::NB * FRAG);
+    const uint32_t loff = lane * 16;
+    auto ldfrag = [&](const uint16_t *fb, size_t frag) {
+        return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(fb + frag * FRAG) + loff);
+    };
+    const uint32_t rowV = (uint32_t)c.H * c.dv * 2;
+    const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
+
+    if (srole) {
+        // ------------------------------------------------------------ S waves
+        const int rbase = (w / C::CG) * C::RPW, cbase = (w % C::CG) * C::CPW;
+        // V slices go through registers (plain loads, written to LDS at the
+        // end of the chunk): with no direct-to-LDS load outstanding, the
+        // compiler's waits for the K~ fragments stay exact
+        u32x4 vreg[C::NV];
+        auto load_v = [&](int ci) {
+            ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+            for (int i = 0; i < C::NV; ++i) {
+                const int unit = i * C::NW + w;
+                const int byte = unit * 1024 + lane * 16;
+                const int row = byte / C::VROW, phys = (byte % C::VROW) >> 4;
+                vreg[i] = *reinterpret_cast<const u32x4 *>(vb + (uint32_t)(ci * BC + row) * rowV + (phys ^ C::swz_v(row)) * 16);
+            }
+        };
+        auto store_v = [&](char *dst) {
+#pragma unroll
+            for (int i = 0; i < C::NV; ++i) *reinterpret_cast<u32x4 *>(dst + (i * C::NW + w) * 1024 + lane * 16) = vreg[i];
+        };
+        bf16x8 kr[C::RPW][C::R];
+        auto load_kp_k = [&](int ci, int kb) {
+            ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+                kr[rt][kb % C::R] = ldfrag(kfb, (size_t)(ci * C::RT + rbase + rt) * C::NB + kb);
+        };
+        f32x4 S[C::RPW][C::CPW];
+        const size_t sbase = (size_t)pair * DK * c.dv + col0;
+        const size_t ebase = (size_t)pair * a.nseg * DK * c.dv + col0;
+        {
+            const float gseg = exp2f((float)(BC * a.seglen) * lg);
+            const float f0 = exp2f(-(float)(BC * ph) * lg);
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                        float x = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
+                        for (int gg = 0; gg < seg; ++gg)
+                            x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
+                        S[rt][ct][r] = x * f0;
+                    }
+        }
+        auto write_st = [&](__bf16 *St) {
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) {
+                    const int row = (rbase + rt) * 16 + 4 * g, col = (cbase + ct) * 16 + l16;
+                    bf16x4 v4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v4[r] = static_cast<__bf16>(S[rt][ct][r]);
+                    *reinterpret_cast<bf16x4 *>(St + col * C::SP + row) = v4;
+                }
+        };
+        write_st(St0);
+        if (i1 > i0) {
+            load_v(i0);
+#pragma unroll
+            for (int kb = 0; kb < C::R; ++kb) load_kp_k(i0, kb);
+            store_v(Vb0);
+        }
+        auto chunk = [&](int ci, const char *Vc, char *Vn, __bf16 *Sn) {
+            __syncthreads();
+            load_v(ci + 1);
+            {
+                const int j = ci % period;
+                if (j == 0) {
+                    const float f = exp2f((float)(BC * (1 + ph)) * lg);
+#pragma unroll
+                    for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * f;
+                }
+                ph = j;
+            }
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const int nb = kb + C::R;
+                const int ci2 = ci + nb / C::NB, kb2 = nb % C::NB;
+                bf16x8 bv[C::CPW];
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) {
+                    const int col = (cbase + ct) * 16 + 4 * (l16 & 3);
+                    bv[ct] = cat(lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col)),
+                                 lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col)));
+                }
+#pragma unroll
+                for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = mfma16(kr[rt][kb % C::R], bv[ct], S[rt][ct]);
+                // the next chunk's fragments of this block are loaded here,
+                // a chunk ahead of their use (nothing moves across)
+                sched_fence();
+                load_kp_k(ci2, kb2);
+                sched_fence();
+            }
+            store_v(Vn);
+            write_st(Sn);
+        };
+        for (int ci = i0; ci < i1; ci += 2) {
+            chunk(ci, Vb0, Vb1, St1);
+            if (ci + 1 < i1) chunk(ci + 1, Vb1, Vb0, St0);
+        }
+        if (a.s_out && seg == a.nseg - 1) {
+            const float f = exp2f((float)(BC * ph) * lg);
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                        a.s_out[sbase + (size_t)row * c.dv + col] = S[rt][ct][r] * f;
+                    }
+        }
+    } else {
+        // ------------------------------------------------------------ O waves
+        int qt[C::NQT];
+#pragma unroll
+        for (int i = 0; i < C::NQT; ++i) qt[i] = C::qtile(w, i);
+        bf16x8 qr[C::NQT][C::KS];
+        bf16x8 pr[C::NQT][C::R];
+        auto load_q = [&](int ci, int f0, int f1) {
+            ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+            for (int f = 0; f < C::NQ; ++f)
+                if (f >= f0 && f < f1)
+                    qr[f / C::KS][f % C::KS] = ldfrag(qfb, (size_t)(ci * C::NKT + qt[f / C::KS]) * C::KS + f % C::KS);
+        };
+        // P^T fragments of the key blocks a query tile reaches (the others
+        // are neither written nor used)
+        auto load_kp_p = [&](int ci, int kb) {
+            ci = ci < nch ? ci : nch - 1;
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u)
+                if (32 * kb <= 16 * qt[u] + 15)
+                    pr[u][kb % C::R] = ldfrag(pfb, (size_t)(ci * C::NKT + qt[u]) * C::NB + kb);
+        };
+        uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 4 * g;
+        float2 *sbase_st = a.stats ? a.stats + (size_t)b * c.T * c.H * a.NS + slice : nullptr;
+        uint32_t pend_o[C::NQT][C::CT][2];
+        uint32_t pend_row[C::NQT];
+        float2 pend_stat[C::NQT];
+#pragma unroll
+        for (int u = 0; u < C::NQT; ++u) {
+            pend_row[u] = (uint32_t)(i0 * BC + 16 * qt[u] + l16) * c.H + h;
+            pend_stat[u] = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
+        }
+        const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+        const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+        const int64_t rp0 = (c.flags & MSR_FLAG_DECAY_ROWNORM) ? row_pos0(c, b) : 0;
+        auto flush_u = [&](int u) {
+            uint16_t *dst = obase + pend_row[u] * (uint32_t)c.dv;
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct) {
+                const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
+                *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+            }
+            if (stats_out && g == 0) sbase_st[pend_row[u] * (uint32_t)a.NS] = pend_stat[u];
+        };
+        if (i1 > i0) {
+            load_q(i0, 0, C::NQ);
+#pragma unroll
+            for (int kb = 0; kb < C::R; ++kb) load_kp_p(i0, kb);
+        }
+        f32x4 oacc[C::NQT][C::CT];
+        auto chunk = [&](int ci, const char *Vc, const __bf16 *Sc) {
+            const int t0 = ci * BC;
+            __syncthreads();
+            s16x4 va[2][C::CT][2];  // V^T of blocks kb (even/odd)
+            auto read_va = [&](int kb, s16x4 (&d)[C::CT][2]) {
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) {
+                    const int col = ct * 16 + 4 * (l16 & 3);
+                    d[ct][0] = lds_tr(Vc + C::voff(32 * kb + 4 * g + (l16 >> 2), col));
+                    d[ct][1] = lds_tr(Vc + C::voff(32 * kb + 16 + 4 * g + (l16 >> 2), col));
+                }
+            };
+            {
+                constexpr int FD = C::KS >= 3 ? 2 : 1;  // S^T fragments read FD k-steps ahead
+                bf16x8 fr[FD + 1][C::CT];
+                auto read_fr = [&](int ks, bf16x8 (&d)[C::CT]) {
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        d[ct] = *reinterpret_cast<const bf16x8 *>(Sc + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g);
+                };
+#pragma unroll
+                for (int ks = 0; ks < FD; ++ks) read_fr(ks, fr[ks]);
+                read_va(0, va[0]);
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    if (ks + FD < C::KS) read_fr(ks + FD, fr[(ks + FD) % (FD + 1)]);
+                    vmem_fence();
+#pragma unroll
+                    for (int u = 0; u < C::NQT; ++u)
+#pragma unroll
+                        for (int ct = 0; ct < C::CT; ++ct)
+                            oacc[u][ct] = mfma16(fr[ks % (FD + 1)][ct], qr[u][ks],
+                                                 ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[u][ct]);
+                    vmem_fence();
+                    if (ks < C::NQT) flush_u(ks);
+                    vmem_fence();
+                }
+#pragma unroll
+                for (int i = C::KS; i < C::NQT; ++i) flush_u(i);
+                vmem_fence();
+            }
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const int nb = kb + C::R;
+                const int ci2 = ci + nb / C::NB, kb2 = nb % C::NB;
+                if (kb + 1 < C::NB) read_va(kb + 1, va[(kb + 1) & 1]);
+#pragma unroll
+                for (int u = 0; u < C::NQT; ++u) {
+                    if (!(32 * kb <= 16 * qt[u] + 15)) continue;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+                        oacc[u][ct] = mfma16(cat(va[kb & 1][ct][0], va[kb & 1][ct][1]), pr[u][kb % C::R], oacc[u][ct]);
+                }
+                sched_fence();
+                load_kp_p(ci2, kb2);
+                load_q(ci + 1, C::qpart0(kb), C::qpart0(kb + 1));
+                sched_fence();
+            }
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u) {
+                const int jq = 16 * qt[u] + l16;
+                pend_row[u] = (uint32_t)(t0 + jq) * c.H + h;
+                if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+                    const float f = 1.f / decay_row_sum(rp0 + t0 + jq, lg);
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * f;
+                }
+                if (norm_here || stats_out) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct) sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
+                    const float mean = sum_lane_groups(sum) * (1.f / W);
+                    float m2 = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) m2 += (oacc[u][ct][r] - mean) * (oacc[u][ct][r] - mean);
+                    m2 = sum_lane_groups(m2);
+                    pend_stat[u] = make_float2(mean, m2);
+                    if (norm_here) {
+                        const float inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
+#pragma unroll
+                        for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) oacc[u][ct][r] = (oacc[u][ct][r] - mean) * inv;
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < C::CT; ++ct) {
+                    pend_o[u][ct][0] = pack_bf16x2(oacc[u][ct][0], oacc[u][ct][1]);
+                    pend_o[u][ct][1] = pack_bf16x2(oacc[u][ct][2], oacc[u][ct][3]);
+                }
+            }
+        };
+        for (int ci = i0; ci < i1; ci += 2) {
+            chunk(ci, Vb0, St0);
+            if (ci + 1 < i1) chunk(ci + 1, Vb1, St1);
+        }
+        if (i1 > i0) {
+#pragma unroll
+            for (int u = 0; u < C::NQT; ++u) flush_u(u);
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
 }
 
@@ -1099,8 +1440,13 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, co
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     main_kernel_begin(st);
-    auto ck = chunk_mfma_kernel<DK, BC, false>;
-    hipLaunchKernelGGL(ck, dim3(grid), dim3(C::THREADS), 0, st, c, a);
+    if constexpr (C::NW == 4 && C::QSTAGE) {
+        auto ck = chunk_ws_kernel<DK, BC>;
+        hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
+    } else {
+        auto ck = chunk_mfma_kernel<DK, BC, false>;
+        hipLaunchKernelGGL(ck, dim3(grid), dim3(C::THREADS), 0, st, c, a);
+    }
     e = hipGetLastError();
     main_kernel_end(st);
     return e;
