@@ -155,12 +155,24 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     kern_ms = [ev.elapsed_ms(i) for i in range(steps)]
     ev.close()
     ms = total_ms / steps
+    # the same call with the split-scores precision option
+    wss = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, chunk,
+                                         flags=msr.MSR_FLAG_SPLIT_SCORES), dtype=torch.uint8, device=dev)
+    msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=wss, flags=msr.MSR_FLAG_SPLIT_SCORES)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=wss, flags=msr.MSR_FLAG_SPLIT_SCORES)
+    t1.record()
+    torch.cuda.synchronize()
+    split_ms = t0.elapsed_time(t1) / steps
+    del wss
     kms = float(np.mean(kern_ms))
     flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     kflops = chunk_kernel_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     return {
         "workload": w, "chunk": chunk, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
-        "kernel_ms": kms, "flops": flops, "kernel_flops": kflops,
+        "kernel_ms": kms, "flops": flops, "kernel_flops": kflops, "split_scores_ms": split_ms,
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
         "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
     }
@@ -452,6 +464,8 @@ def main():
                      "traffic": traffic, "kernel": main_kernel,
                      "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["kernel_flops"]},
         "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+        "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",
+                         "ms_per_step": r["split_scores_ms"]},
         "cpu_baseline": cpu,
         "decode": dec,
         "parallel": par,

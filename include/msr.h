@@ -95,7 +95,22 @@ typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
  * call.  The factor multiplies the row's output before GroupNorm, which
  * therefore sees it only through eps.
  */
-enum { MSR_FLAG_NO_ROTATE = 1u, MSR_FLAG_NO_GROUPNORM = 2u, MSR_FLAG_DECAY_ROWNORM = 4u };
+/*
+ * SPLIT_SCORES (a precision option of the bf16 matrix-core path of
+ * msr_chunkwise; other paths compute the scores in fp32 and ignore it): the
+ * intra-chunk scores q~ . k~ are taken from two-term bf16 splits of the fp32
+ * rotated Q and K (hi.hi + lo.hi + hi.lo) instead of their bf16 roundings.
+ * A score much smaller than |q~||k~| otherwise loses its relative accuracy,
+ * which GroupNorm amplifies on rows dominated by few tokens -- under strong
+ * decay (gamma of about 0.5 or less) enough to reach the bf16 tolerance.
+ * Costs a rotation pass and three score products instead of one.
+ */
+enum {
+    MSR_FLAG_NO_ROTATE = 1u,
+    MSR_FLAG_NO_GROUPNORM = 2u,
+    MSR_FLAG_DECAY_ROWNORM = 4u,
+    MSR_FLAG_SPLIT_SCORES = 8u
+};
 
 /* forms, for msr_workspace_size */
 enum {

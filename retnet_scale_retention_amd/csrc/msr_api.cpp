@@ -62,7 +62,8 @@ msr_status check_problem(const msr_problem *p, bool T1) {
         return fail(MSR_ERR_INVALID_ARG, "positions beyond 2^40 are not supported");
     if (p->pos_rows && (reinterpret_cast<uintptr_t>(p->pos_rows) & 7u))
         return fail(MSR_ERR_INVALID_ARG, "pos_rows is not 8-byte aligned");
-    if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM | MSR_FLAG_DECAY_ROWNORM))
+    if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM | MSR_FLAG_DECAY_ROWNORM |
+                               MSR_FLAG_SPLIT_SCORES))
         return fail(MSR_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     return MSR_OK;
 }
@@ -384,6 +385,44 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     return e;
 }
 
+// ---- split scores (MSR_FLAG_SPLIT_SCORES) ----------------------------------
+
+bool split_scores(const msr_problem *p, int chunk) {
+    return (p->flags & MSR_FLAG_SPLIT_SCORES) && p->T > MSR_DECODE_MAX_T &&
+           mfma_supported(p, MSR_FORM_CHUNKWISE, chunk);
+}
+
+// workspace in front of the chunkwise workspace: Q~ and K~ (scaled) as hi, lo bf16 pairs
+struct SplitPlan {
+    size_t qh = 0, ql = 0, kh = 0, kl = 0, total = 0;
+};
+
+SplitPlan split_plan(const msr_problem *p) {
+    SplitPlan b;
+    const size_t t = round_up((size_t)p->B * p->T * p->H * p->dk * 2);
+    b.qh = 0;
+    b.ql = t;
+    b.kh = 2 * t;
+    b.kl = 3 * t;
+    b.total = 4 * t;
+    return b;
+}
+
+hipError_t chunkwise_split(const msr_problem *p, int chunk, const void *Q, const void *K, const void *V, void *O,
+                           const float *s_in, float *s_out, void *ws, hipStream_t st) {
+    const MsrConst c = make_const(p, chunk);
+    const SplitPlan b = split_plan(p);
+    char *w = static_cast<char *>(ws);
+    hipError_t e = launch_rotate_tok(c, Q, MSR_BF16, w + b.qh, MSR_BF16, 1.f, 1.f, st, w + b.ql);
+    if (e == hipSuccess) e = launch_rotate_tok(c, K, MSR_BF16, w + b.kh, MSR_BF16, c.scale, 1.f, st, w + b.kl);
+    if (e != hipSuccess) return e;
+    msr_problem sub = *p;  // rotated and scaled already; positions stay for the row factors
+    sub.flags |= MSR_FLAG_NO_ROTATE;
+    sub.scale = 1.f;
+    return mfma_chunkwise(make_const(&sub, chunk), &sub, chunk, w + b.qh, w + b.kh, V, O, s_in, s_out, w + b.total,
+                          st, w + b.ql, w + b.kl);
+}
+
 // ---- Q/K/V projections -------------------------------------------------
 
 // the chunkwise problem over projected inputs: rotation and scale already applied
@@ -476,7 +515,8 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
         return fail(MSR_ERR_INVALID_ARG, "unknown form %d", form);
     }
     size_t need = generic_plan(p, form, chunk).total;
-    const size_t mf = mfma_workspace_bytes(p, form, chunk);
+    size_t mf = mfma_workspace_bytes(p, form, chunk);
+    if (form == MSR_FORM_CHUNKWISE && split_scores(p, chunk)) mf += split_plan(p).total;
     if (mf > need) need = mf;
     *bytes = need;
     return MSR_OK;
@@ -540,6 +580,8 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     if (p->B == 0) return MSR_OK;
     if (p->T == 0) return hip_status(launch_copy_state(c, state_in, state_out, st), "copy state");
 
+    if (split_scores(p, chunk))
+        return hip_status(chunkwise_split(p, chunk, Q, K, V, O, state_in, state_out, ws, st), "split chunkwise");
     if (mfma_supported(p, MSR_FORM_CHUNKWISE, chunk))
         return hip_status(mfma_chunkwise(c, p, chunk, Q, K, V, O, state_in, state_out, ws, st),
                           "mfma chunkwise");

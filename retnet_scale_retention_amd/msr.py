@@ -18,7 +18,7 @@ LIB_PATH = Path(os.environ.get("MSR_LIB", Path(__file__).resolve().parent / "lib
 
 MSR_OK = 0
 MSR_F32, MSR_BF16 = 0, 1
-MSR_FLAG_NO_ROTATE, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_DECAY_ROWNORM = 1, 2, 4
+MSR_FLAG_NO_ROTATE, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_DECAY_ROWNORM, MSR_FLAG_SPLIT_SCORES = 1, 2, 4, 8
 MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD, MSR_FORM_QKV_CHUNKWISE = 0, 1, 2, 3, 4
 STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_ERR_DTYPE",
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}

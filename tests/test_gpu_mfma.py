@@ -198,3 +198,44 @@ def test_mfma_parallel_state_out_aliases_state_in():
     torch.cuda.synchronize()
     assert s2.data_ptr() == sd.data_ptr()
     assert out_err(down(o), ro) < TOL["bf16"] and state_err(down(sd), rs) < TOL["bf16"]
+
+
+# strong decay: rows dominated by a few tokens, where bf16-rounded q~, k~
+# lose the relative accuracy of small scores (the split-scores option)
+STRONG = [  # (B, T, H, dk, dv, chunk)
+    (2, 256, 2, 64, 128, 64),
+    (1, 256, 2, 256, 512, 128),
+    (1, 512, 2, 128, 64, 256),
+    (1, 512, 1, 256, 128, 256),   # Q~ not staged in LDS by the prep kernel at d_k = b = 256
+]
+
+
+@pytest.mark.parametrize("case", STRONG, ids=lambda c: "B%dT%dH%ddk%ddv%db%d" % c)
+@pytest.mark.parametrize("gamma", [0.5, 0.25])
+def test_mfma_split_scores_strong_decay(case, gamma):
+    B, T, H, dk, dv, chunk = case
+    import retnet_scale_retention_amd as msr
+    w = mi.Workload("strong", 80, B, T, H, dk, dv, "bf16", (chunk,))
+    q, k, v = mi.qkv(w)
+    g = np.full(H, gamma, np.float32)
+    s_in = mi.state(w, 0.5)
+    ro, rs = orc.chunkwise(q, k, v, g, chunk, s_in=s_in, pos0=9)
+    o1, s1 = run(q, k, v, g, chunk, s_in=s_in, pos0=9)
+    o2, s2 = run(q, k, v, g, chunk, s_in=s_in, pos0=9, flags=msr.MSR_FLAG_SPLIT_SCORES)
+    e1, e2 = out_err(o1, ro), out_err(o2, ro)
+    note(f"gamma={gamma}: O err {e1:.2e} plain, {e2:.2e} split scores; state err {state_err(s2, rs):.2e}")
+    assert e2 < TOL["bf16"] and state_err(s2, rs) < TOL["bf16"]
+    assert e2 <= e1 * 1.05
+
+
+@pytest.mark.parametrize("flags", [2, 4, 6])  # no GroupNorm / row-normalised decay / both
+def test_mfma_split_scores_with_flags(flags):
+    import retnet_scale_retention_amd as msr
+    w = mi.Workload("split-flags", 81, 2, 256, 2, 64, 128, "bf16", (64,))
+    q, k, v = mi.qkv(w)
+    g = mi.gammas(2)
+    ro, _ = orc.chunkwise(q, k, v, g, 64, pos0=3, groupnorm=not (flags & 2), rownorm=bool(flags & 4))
+    o, _ = run(q, k, v, g, 64, pos0=3, flags=flags | msr.MSR_FLAG_SPLIT_SCORES)
+    e = out_err(o, ro)
+    note(f"split scores, flags {flags}: O err {e:.2e}")
+    assert e < TOL["bf16"]
