@@ -94,6 +94,41 @@ __global__ void rotate_tok_kernel(MsrConst c, const TIn *__restrict__ x, TOut *_
     }
 }
 
+// The same, four pairs (8 elements, one or two 16-byte accesses) per work
+// item; d_k a multiple of 8
+template <typename TIn, typename TOut>
+__global__ void rotate_tok8_kernel(MsrConst c, const TIn *__restrict__ x, TOut *__restrict__ y,
+                                   TOut *__restrict__ ylo, float factor, float sign) {
+    const int g8 = c.dk / 8;
+    const size_t n = (size_t)c.B * c.T * c.H * g8;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const int i0 = (int)(e % g8) * 4;  // first pair
+        const size_t r = e / g8;           // (b T + t) H + h
+        const int t = (int)((r / c.H) % c.T), b = (int)(r / ((size_t)c.H * c.T));
+        float v[8], hi[8], lo[8];
+        ldv<8>(x + 8 * e, v);
+        const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
+        const int64_t pos = rot ? row_pos0(c, b) + t : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float cs = 1.f, sn = 0.f;
+            if (rot) rot_cos_sin(pos, c.theta[i0 + q], cs, sn);
+            sn *= sign;
+            const float x0 = v[2 * q], x1 = v[2 * q + 1];
+            hi[2 * q] = (x0 * cs - x1 * sn) * factor;
+            hi[2 * q + 1] = (x1 * cs + x0 * sn) * factor;
+        }
+        if constexpr (sizeof(TOut) == 2) {
+            if (ylo) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) lo[j] = hi[j] - bf16_to_f32(f32_to_bf16(hi[j]));
+                stv<8>(ylo + 8 * e, lo);
+            }
+        }
+        stv<8>(y + 8 * e, hi);
+    }
+}
+
 // GroupNorm backward, one wave per (token, head) row of d_v values:
 //   y = (x - mean) s,  s = 1/sqrt(var + eps),
 //   dx = s (dy - mean(dy) - y mean(dy y))
@@ -280,6 +315,16 @@ hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, in
                          float sign, hipStream_t st) {
     const size_t n = (size_t)c.B * c.T * c.H * (c.dk / 2);
     if (n == 0) return hipSuccess;
+    if (c.dk % 8 == 0) {
+        const size_t n8 = n / 4;
+        if (out_dtype == MSR_BF16)
+            hipLaunchKernelGGL((rotate_tok8_kernel<TIn, uint16_t>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
+                               static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign);
+        else
+            hipLaunchKernelGGL((rotate_tok8_kernel<TIn, float>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
+                               static_cast<float *>(y), nullptr, factor, sign);
+        return hipGetLastError();
+    }
     if (out_dtype == MSR_BF16)
         hipLaunchKernelGGL((rotate_tok_kernel<TIn, uint16_t>), dim3(grid_for(n)), dim3(256), 0, st, c, x,
                            static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign);
