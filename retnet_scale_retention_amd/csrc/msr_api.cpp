@@ -235,6 +235,10 @@ msr_problem mfma_sub(const msr_problem *p, int d1, int d2) {
     return r;
 }
 
+// The retention calls of the backward pass may use any chunk size (the forms
+// agree for every b); 64 runs fastest on the MFMA path.
+int backward_chunk(const msr_problem *p, int chunk) { return p->T % 64 == 0 ? 64 : chunk; }
+
 bool mfma_backward_ok(const msr_problem *p, int chunk) {
     if (p->dtype != MSR_BF16 || p->dv % 64 != 0) return false;
     int off[kMaxParts], len[kMaxParts];
@@ -498,7 +502,8 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
         if (chunk < 1) return fail(MSR_ERR_SHAPE, "chunk=%d must be >= 1", chunk);
         if (p->dv > MSR_MAX_DK)
             return fail(MSR_ERR_UNSUPPORTED, "the backward pass needs dv <= %d (dv=%d)", MSR_MAX_DK, p->dv);
-        *bytes = mfma_backward_ok(p, chunk) ? back_plan_mfma(p, chunk).total : back_plan(p, chunk).total;
+        const int bc = backward_chunk(p, chunk);
+        *bytes = mfma_backward_ok(p, bc) ? back_plan_mfma(p, bc).total : back_plan(p, chunk).total;
         return MSR_OK;
     }
     if (form == MSR_FORM_QKV_CHUNKWISE) {
@@ -673,8 +678,9 @@ msr_status msr_chunkwise_backward(const msr_problem *p, int32_t chunk, const voi
         if (!dstate_in) return MSR_OK;
         return hip_status(launch_state_op(c, dk, dv, dstate_out, dstate_in, 0, 0.f, 0, dv, st), "backward");
     }
-    if (mfma_backward_ok(p, chunk))
-        return hip_status(backward_mfma(p, chunk, Q, K, V, state_in, dO, dstate_out, dQ, dK, dV, dstate_in, ws, st),
+    if (mfma_backward_ok(p, backward_chunk(p, chunk)))
+        return hip_status(backward_mfma(p, backward_chunk(p, chunk), Q, K, V, state_in, dO, dstate_out, dQ, dK, dV,
+                                        dstate_in, ws, st),
                           "backward (mfma)");
     const BackPlan b = back_plan(p, chunk);
     char *w = static_cast<char *>(ws);
