@@ -634,9 +634,9 @@ msr_status msr_qkv_chunkwise(const msr_problem *p, int32_t chunk, int32_t d_mode
     if (s != MSR_OK) return s;
     size_t need = 0;
     if ((s = msr_workspace_size(p, MSR_FORM_QKV_CHUNKWISE, chunk, &need)) != MSR_OK) return s;
-    if (!ws || ws_bytes < need)
+    if (need > 0 && (!ws || ws_bytes < need))
         return fail(MSR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
-    if (!aligned16(ws)) return fail(MSR_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+    if (ws && !aligned16(ws)) return fail(MSR_ERR_INVALID_ARG, "ws is not 16-byte aligned");
     const QkvPlan b = qkv_plan(p);
     char *w = static_cast<char *>(ws);
     const msr_problem sub = qkv_sub(p);

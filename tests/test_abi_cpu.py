@@ -151,6 +151,18 @@ def test_qkv_calls_validate_before_any_launch():
     assert m.STATUS[s] == "MSR_ERR_WORKSPACE"
 
 
+def test_empty_problems_need_no_workspace_and_launch_nothing():
+    lib = msr.load()
+    null = ctypes.c_void_p()
+    d = desc(B=0)
+    s = lib.msr_qkv_chunkwise(d.ref, 16, 64, null, null, null, null, null, null, null, null, 0, null)
+    assert m.STATUS[s] == "MSR_OK", lib.msr_last_error().decode()
+    s = lib.msr_qkv_projection(d.ref, 64, null, null, null, null, null, null, null, null)
+    assert m.STATUS[s] == "MSR_OK"
+    s = lib.msr_chunkwise(d.ref, 16, null, null, null, null, null, null, null, 0, null)
+    assert m.STATUS[s] == "MSR_OK"
+
+
 def test_null_problem_and_bytes():
     lib = msr.load()
     n = ctypes.c_size_t(0)
