@@ -21,6 +21,7 @@ already resident in HBM.  The same JSON line also reports
   - backward: msr_chunkwise_backward on the small and the 7B-shaped layers;
   - qkv: the Q/K/V projections (d_model = 4096) with the rotation in the
     GEMM epilogue, and the projections + chunkwise form together;
+  - other_chunk: the same forward at the workload's other chunk size (256);
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
@@ -167,12 +168,27 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     torch.cuda.synchronize()
     split_ms = t0.elapsed_time(t1) / steps
     del wss
+    # the other chunk size of the 7B-shaped workload
+    ochunk = 256 if chunk != 256 else 128
+    wso = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, ochunk),
+                      dtype=torch.uint8, device=dev)
+    msr.msr_chunkwise(qd, kd, vd, g, ochunk, out=o, state_out=s, workspace=wso)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        msr.msr_chunkwise(qd, kd, vd, g, ochunk, out=o, state_out=s, workspace=wso)
+    t1.record()
+    torch.cuda.synchronize()
+    other_ms = t0.elapsed_time(t1) / steps
+    del wso
     kms = float(np.mean(kern_ms))
     flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     kflops = chunk_kernel_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     return {
         "workload": w, "chunk": chunk, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
         "kernel_ms": kms, "flops": flops, "kernel_flops": kflops, "split_scores_ms": split_ms,
+        "other_chunk": {"chunk": ochunk, "ms_per_step": other_ms, "tokens_per_s": w.B * w.T / (other_ms / 1e3),
+                        "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, ochunk) / (other_ms / 1e3) / 1e12},
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
         "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
     }
@@ -466,6 +482,7 @@ def main():
         "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
         "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",
                          "ms_per_step": r["split_scores_ms"]},
+        "other_chunk": r["other_chunk"],
         "cpu_baseline": cpu,
         "decode": dec,
         "parallel": par,
