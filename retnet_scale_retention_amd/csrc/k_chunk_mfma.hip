@@ -48,6 +48,7 @@
 // use, so the loads have most of a chunk to land.  Every wave issues the same
 // loads in the same order each chunk, so one fixed vmcnt wait tells when the
 // next V slice has landed.
+#include "msr_chunk.hpp"
 #include "msr_device.hpp"
 #include "msr_mfma.hpp"
 
@@ -133,18 +134,6 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// The chunk kernel carries S^ = S gamma^(-b j) instead of the state S, where
-// j = (chunk index) mod m: within a run of m chunks the update is then a
-// plain accumulation S^ += gamma^(-b j) K~^T (V (.) zeta) (the factor rides
-// on the K~^T fragments), and S^ is multiplied by a power of gamma only when
-// a run starts.  m is the largest period with gamma^(-b (m-1)) <= 2^40, so S^
-// stays far from the fp32 range limits; gamma = 1 never rescales.
-__device__ __forceinline__ int rescale_period(float lg, int bc) {
-    const float per = (float)bc * -lg;  // -log2(gamma^b) >= 0
-    const float m = per > 0.f ? 40.f / per + 1.f : 1e9f;
-    return m >= (float)(1 << 30) ? (1 << 30) : (int)m;
-}
-
 template <int DK, int BC>
 struct Cfg {
     static constexpr int NKT = BC / 16;        // 16-token tiles per chunk
@@ -209,19 +198,6 @@ struct Cfg {
     }
 };
 
-struct ChunkArgs {
-    const uint16_t *qf, *kf, *pf;  // fragments written by prep_kernel
-    const uint16_t *v;
-    uint16_t *o;
-    const float *s_in;
-    float *s_out;
-    float2 *stats;  // [B*T*H][NS] (mean, M2) of each slice, when NS > 1
-    int NS;         // slices per pair (dv / W)
-    int nseg, seglen;  // segments of seglen chunks per pair (nseg * seglen = T / b)
-    float *segE;       // [pair][nseg][dk][dv] end state of each segment from a zero state
-    int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
-};
-
 // Per (pair, chunk): rotation of the chunk's Q and K rows (theta_shift,
 // jsqmd.com s2: pair i of the token at position p becomes
 // (x0 c - x1 s, x1 c + x0 s) with c, s = cos, sin of p theta_i; fp32
@@ -249,7 +225,13 @@ struct ChunkArgs {
 // bf16 splits of more precise operands); the scores then take
 // hi.hi + lo.hi + hi.lo, the lo fragments read straight from global memory.
 // Everything else uses the hi parts.
-template <int DK, int BC, bool PAR, bool SPLIT = false>
+//
+// QPERM: the QF fragments hold their d_k columns in the order
+// {4g..4g+3, 16+4g..16+4g+3} of lane group g within each 32-column step --
+// the rows two 16x16 state tiles leave in each lane, so that a kernel
+// holding the state in MFMA accumulators can feed it to the inter-chunk
+// product without a transpose (k_chunk_wide.hip).
+template <int DK, int BC, bool PAR, bool SPLIT = false, bool QPERM = false>
 __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c, const uint16_t *__restrict__ q,
                                                                   const uint16_t *__restrict__ k,
                                                                   uint16_t *__restrict__ qf, uint16_t *__restrict__ kf,
@@ -263,6 +245,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     constexpr int RPT = BC / RG;                  // rows per run
     constexpr bool QS = C::QSTAGE;
     static_assert(RPT >= 1 && RG * RPT == BC, "row runs");
+    static_assert(!QPERM || (QS && !PAR), "QPERM fragments are formed from the staged Q~ tile");
     static_assert((QS ? 2 : 1) * BC * C::KROW + 2 * BC * 4 <= 163840, "LDS budget (prep kernel)");
     __shared__ __attribute__((aligned(16))) char Ks[BC * C::KROW];            // K~, swizzled rows
     __shared__ __attribute__((aligned(16))) char Qs[QS ? BC * C::KROW : 16];  // Q~, the same layout
@@ -348,7 +331,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
         const int ph = ci == 0 ? 0 : (ci - 1) % rescale_period(lg, BC);
         for (int f = w; f < C::NKT * C::KS; f += PW) {
             const int u = f / C::KS, ks = f % C::KS, row = 16 * u + l16;
-            const u32x4 x = ld16(Qs, C::koff(row, 32 * ks + 8 * g));
+            u32x4 x;
+            if constexpr (QPERM) {
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(Qs + C::koff(row, 32 * ks + 4 * g));
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(Qs + C::koff(row, 32 * ks + 16 + 4 * g));
+                x = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                x = ld16(Qs, C::koff(row, 32 * ks + 8 * g));
+            }
             u32x4 y = x;
             if (!PAR) {
                 const float fq = exp2f((float)(row + 1 + BC * ph) * lg);
@@ -1366,16 +1356,18 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     }
 }
 
-// GroupNorm of rows whose slices wrote (mean, M2) statistics over W values
-// each: the row's mean is the mean of the slice means and its M2 the sum of
-// the slice M2 plus W (slice mean - row mean)^2 (the pairwise-update formula
-// of Chan, Golub and LeVeque for equal counts).  A thread normalises 32
+// GroupNorm of rows whose NS slices wrote (mean, M2) statistics over
+// n = d_v / NS values each: the row's mean is the mean of the slice means and
+// its M2 the sum of the slice M2 plus n (slice mean - row mean)^2 (the
+// pairwise-update formula of Chan, Golub and LeVeque for equal counts).  A thread normalises 32
 // values of one row in place (four 16-byte pieces, d_v / 32 threads per row)
-// and combines that row's statistics itself; O is streamed with
-// non-temporal loads and stores.
+// and combines that row's statistics (over a butterfly of lane exchanges
+// among the row's threads when their count is a power of two); O is
+// streamed with non-temporal loads and stores.
 __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, const float2 *__restrict__ stats,
                                                           uint16_t *__restrict__ o, size_t rows) {
-    const int tpr = c.dv / 32;  // threads per row
+    const int tpr = c.dv / 32;            // threads per row
+    const float wn = (float)(c.dv / NS);  // values per slice
     const size_t gid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     const size_t row = gid / tpr;
     const int j = (int)(gid % tpr);
@@ -1385,22 +1377,44 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, co
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = __builtin_nontemporal_load(p + i * tpr);
     const float2 *st = stats + row * NS;
-    float2 sv[MSR_MAX_DV / W];
-    float mean = 0.f;
-#pragma unroll
-    for (int s = 0; s < MSR_MAX_DV / W; ++s)
-        if (s < NS) {
-            sv[s] = st[s];
-            mean += sv[s].x;
+    float mean = 0.f, m2 = 0.f;
+    if ((tpr & (tpr - 1)) == 0 && NS <= tpr) {
+        // the row's tpr threads are consecutive lanes of one wave (tpr is a
+        // power of two <= 32): thread j takes slice j (if any) and the
+        // partials combine pairwise over a butterfly of lane exchanges
+        float n = 0.f;
+        if (j < NS) {
+            const float2 sj = st[j];
+            n = wn;
+            mean = sj.x;
+            m2 = sj.y;
         }
-    mean /= (float)NS;
-    float m2 = 0.f;
-#pragma unroll
-    for (int s = 0; s < MSR_MAX_DV / W; ++s)
-        if (s < NS) {
-            const float d = sv[s].x - mean;
-            m2 += sv[s].y + (float)W * d * d;
+        for (int off = 1; off < tpr; off <<= 1) {
+            const float nb = __shfl_xor(n, off), mb = __shfl_xor(mean, off), m2b = __shfl_xor(m2, off);
+            const float nn = n + nb;
+            if (nn > 0.f) {
+                const float d = mb - mean, fb = nb / nn;
+                mean += d * fb;
+                m2 += m2b + d * d * n * fb;
+            }
+            n = nn;
         }
+    } else {
+        float2 sv[MSR_MAX_DV / 32];
+#pragma unroll
+        for (int s = 0; s < MSR_MAX_DV / 32; ++s)
+            if (s < NS) {
+                sv[s] = st[s];
+                mean += sv[s].x;
+            }
+        mean /= (float)NS;
+#pragma unroll
+        for (int s = 0; s < MSR_MAX_DV / 32; ++s)
+            if (s < NS) {
+                const float d = sv[s].x - mean;
+                m2 += sv[s].y + wn * d * d;
+            }
+    }
     const float inv = 1.f / sqrtf(m2 / (float)c.dv + c.eps);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1413,27 +1427,46 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, co
     }
 }
 
-template <int DK, int BC>
-hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, const void *Qlo,
-                        const void *Klo, hipStream_t st) {
-    const int npairs = c.B * c.H;
+template <int DK, int BC, bool QPERM>
+void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, const void *Qlo,
+                 const void *Klo, hipStream_t st) {
     using C = Cfg<DK, BC>;
+    const unsigned grid = (unsigned)(c.B * c.H * (c.T / BC));
     if (Qlo && Klo) {
-        auto pk = prep_kernel<DK, BC, false, true>;
-        hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c,
-                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
-                           const_cast<uint16_t *>(a.qf), const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf),
-                           (uint16_t *)nullptr, static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo));
+        auto pk = prep_kernel<DK, BC, false, true, QPERM>;
+        hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
+                           static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
+                           const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
+                           static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo));
     } else {
-        auto pk = prep_kernel<DK, BC, false>;
-        hipLaunchKernelGGL(pk, dim3(npairs * (c.T / BC)), dim3(C::PREP_NT), 0, st, c,
-                           static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
-                           const_cast<uint16_t *>(a.qf), const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf),
-                           (uint16_t *)nullptr, (const uint16_t *)nullptr, (const uint16_t *)nullptr);
+        auto pk = prep_kernel<DK, BC, false, false, QPERM>;
+        hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
+                           static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
+                           const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
+                           (const uint16_t *)nullptr, (const uint16_t *)nullptr);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int grid = npairs * a.nseg * a.NS;
+}
+
+template <int DK, int BC>
+hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, bool wide, const void *Q, const void *K,
+                        const void *Qlo, const void *Klo, hipStream_t st) {
+    using C = Cfg<DK, BC>;
+    hipError_t e = hipSuccess;
+    if constexpr (C::QSTAGE && BC == 64 && DK >= 128) {
+        if (wide) {  // 256-column slices (k_chunk_wide.hip)
+            launch_prep<DK, BC, true>(c, a, Q, K, Qlo, Klo, st);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (a.nseg > 1 && (e = launch_chunk_wide(c, a, BC, true, st)) != hipSuccess) return e;
+            main_kernel_begin(st);
+            e = launch_chunk_wide(c, a, BC, false, st);
+            main_kernel_end(st);
+            return e;
+        }
+    }
+    if (wide) return hipErrorNotSupported;
+    launch_prep<DK, BC, false>(c, a, Q, K, Qlo, Klo, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int grid = c.B * c.H * a.nseg * a.NS;
     if (a.nseg > 1) {  // end states of segments 0 .. nseg-2
         auto sk = chunk_mfma_kernel<DK, BC, true>;
         hipLaunchKernelGGL(sk, dim3(grid), dim3(C::THREADS), 0, st, c, a);
@@ -1453,12 +1486,12 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, const void *Q, co
 }
 
 template <int DK>
-hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, const void *Q, const void *K,
+hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, bool wide, int chunk, const void *Q, const void *K,
                        const void *Qlo, const void *Klo, hipStream_t st) {
     switch (chunk) {
-    case 64: return launch_chunk<DK, 64>(c, a, Q, K, Qlo, Klo, st);
-    case 128: return launch_chunk<DK, 128>(c, a, Q, K, Qlo, Klo, st);
-    case 256: return launch_chunk<DK, 256>(c, a, Q, K, Qlo, Klo, st);
+    case 64: return launch_chunk<DK, 64>(c, a, wide, Q, K, Qlo, Klo, st);
+    case 128: return launch_chunk<DK, 128>(c, a, wide, Q, K, Qlo, Klo, st);
+    case 256: return launch_chunk<DK, 256>(c, a, wide, Q, K, Qlo, Klo, st);
     default: return hipErrorNotSupported;
     }
 }
@@ -1466,13 +1499,15 @@ hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, int chunk, const v
 struct MfmaPlan {
     size_t qf = 0, kf = 0, pf = 0, stats = 0, segE = 0, total = 0;
     int nseg = 1;
+    int NS = 1;         // GroupNorm partials per row
+    bool wide = false;  // 256-column slices (k_chunk_wide.hip)
 };
 
 // Segments per pair: doubled while the workgroups (pairs x value slices x
 // segments) stay within one per CU and every segment keeps >= 2 chunks.
-int choose_nseg(const msr_problem *p, int chunk) {
+int choose_nseg(const msr_problem *p, int chunk, int slice_cols) {
     const int nch = p->T / chunk;
-    const long units = (long)p->B * p->H * (p->dv / W);
+    const long units = (long)p->B * p->H * (p->dv / slice_cols);
     int g = 1;
     while (units * g * 2 <= 256 && nch % (g * 2) == 0 && nch / (g * 2) >= 2) g *= 2;
     return g;
@@ -1488,9 +1523,10 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     m.pf = m.kf + up(tokens * p->dk * 2);
     // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
     m.stats = m.pf + up(tokens * chunk * 2);
-    const int NS = p->dv / W;
-    m.segE = m.stats + (NS > 1 ? up(tokens * NS * sizeof(float2)) : 0);
-    m.nseg = choose_nseg(p, chunk);
+    m.wide = chunk_wide_supported(p->dk, p->dv, chunk);
+    m.NS = p->dv / (m.wide ? 32 : W);  // GroupNorm partials per row
+    m.segE = m.stats + (m.NS > 1 ? up(tokens * m.NS * sizeof(float2)) : 0);
+    m.nseg = choose_nseg(p, chunk, m.wide ? 256 : W);
     m.total = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
     return m;
 }
@@ -1546,6 +1582,7 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
         a.s_out = s_out;
         a.stats = nullptr;
         a.NS = NS;
+        a.NW2 = NS;
         a.nseg = 1;
         a.seglen = nqb;
         a.segE = nullptr;
@@ -1601,7 +1638,8 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.o = static_cast<uint16_t *>(O);
     a.s_in = s_in;
     a.s_out = s_out;
-    a.NS = p->dv / W;
+    a.NS = m.NS;
+    a.NW2 = m.wide ? p->dv / 256 : a.NS;
     a.stats = a.NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
     a.nseg = m.nseg;
     a.seglen = p->T / chunk / m.nseg;
@@ -1609,9 +1647,9 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
 
     hipError_t e = hipSuccess;
     switch (p->dk) {
-    case 64: e = dispatch_bc<64>(c, a, chunk, Q, K, Qlo, Klo, st); break;
-    case 128: e = dispatch_bc<128>(c, a, chunk, Q, K, Qlo, Klo, st); break;
-    case 256: e = dispatch_bc<256>(c, a, chunk, Q, K, Qlo, Klo, st); break;
+    case 64: e = dispatch_bc<64>(c, a, m.wide, chunk, Q, K, Qlo, Klo, st); break;
+    case 128: e = dispatch_bc<128>(c, a, m.wide, chunk, Q, K, Qlo, Klo, st); break;
+    case 256: e = dispatch_bc<256>(c, a, m.wide, chunk, Q, K, Qlo, Klo, st); break;
     default: e = hipErrorNotSupported;
     }
     if (e != hipSuccess) return e;
