@@ -22,11 +22,13 @@ already resident in HBM.  The same JSON line also reports
   - qkv: the Q/K/V projections (d_model = 4096) with the rotation in the
     GEMM epilogue, and the projections + chunkwise form together;
   - other_chunk: the same forward at the workload's other chunk size (256);
+  - long_sequence: the chunkwise forward over B=1, T=131072, H=8, d_k=128,
+    d_v=256 at chunk 64, 128 and 256 (state carried across all chunks);
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
   python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward]
-                  [--no-qkv] [--copy-mib N]
+                  [--no-qkv] [--no-long] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -99,6 +101,7 @@ def chunk_bytes(T, H, B, dk, dv):
 KERNEL_SOURCES = {
     "chunk_mfma_kernel": "k_chunk_mfma.hip",
     "chunk_ws_kernel": "k_chunk_mfma.hip",
+    "chunk_wide_kernel": "k_chunk_wide.hip",
     "prep_kernel": "k_chunk_mfma.hip",
     "gn_finalize_kernel": "k_chunk_mfma.hip",
     "decode_kernel": "k_decode.hip",
@@ -192,6 +195,38 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
         "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
     }
+
+
+def bench_long(torch, msr, mi, calls):
+    """The long-sequence workload's chunk sweep: one state carried across all
+    chunks of each (batch, head) pair."""
+    w = mi.WORKLOADS["long"]
+    dev = torch.device("cuda:0")
+    q, k, v = mi.qkv(w)
+    up = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    g = mi.gammas(w.H)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    out = {"config": {"B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv}}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    for chunk in w.chunks:
+        ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE,
+                                            chunk), dtype=torch.uint8, device=dev)
+        msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(calls):
+            msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / calls
+        del ws
+        out["b%d" % chunk] = {"ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+                              "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk) / (ms / 1e3) / 1e12}
+    return out
 
 
 def bench_parallel(torch, msr, mi, steps):
@@ -422,6 +457,7 @@ def main():
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -442,6 +478,7 @@ def main():
 
     r = bench_chunkwise(torch, msr, mi, args.steps, args.warmup, args.chunk)
     w = r["workload"]
+    lng = None if args.no_long else bench_long(torch, msr, mi, 3)
     dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
     par = None if args.no_parallel else bench_parallel(torch, msr, mi, 3)
     bwd = None
@@ -457,8 +494,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    # the chunk recurrence runs as the warp-specialised kernel for b <= 128
-    main_kernel = "chunk_ws_kernel" if args.chunk <= 128 else "chunk_mfma_kernel"
+    # the chunk recurrence runs as the wide-slice kernel at b = 64, the
+    # warp-specialised kernel at b = 128 and the single-role kernel at b = 256
+    main_kernel = {64: "chunk_wide_kernel", 128: "chunk_ws_kernel"}.get(args.chunk, "chunk_mfma_kernel")
     traffic = traffic_record(main_kernel)
     line = {
         "metric": "chunkwise MSR fwd tokens/s + decode steps/s; % of bf16 MFMA / HBM peak",
@@ -483,6 +521,7 @@ def main():
         "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",
                          "ms_per_step": r["split_scores_ms"]},
         "other_chunk": r["other_chunk"],
+        "long_sequence": lng,
         "cpu_baseline": cpu,
         "decode": dec,
         "parallel": par,

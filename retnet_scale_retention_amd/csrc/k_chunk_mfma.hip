@@ -1523,7 +1523,7 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     m.pf = m.kf + up(tokens * p->dk * 2);
     // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
     m.stats = m.pf + up(tokens * chunk * 2);
-    m.wide = chunk_wide_supported(p->dk, p->dv, chunk);
+    m.wide = chunk_wide_supported(p->dk, p->dv, chunk) && !(p->flags & kFlagNoWide);
     m.NS = p->dv / (m.wide ? 32 : W);  // GroupNorm partials per row
     m.segE = m.stats + (m.NS > 1 ? up(tokens * m.NS * sizeof(float2)) : 0);
     m.nseg = choose_nseg(p, chunk, m.wide ? 256 : W);

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "msr_internal.hpp"
+#include "msr_chunk.hpp"
 #include "msr_mfma.hpp"
 
 namespace {
@@ -232,6 +233,7 @@ int dv_parts(int dv, int *off, int *len) {
 msr_problem mfma_sub(const msr_problem *p, int d1, int d2) {
     msr_problem r = retention_problem(p, d1, d2);
     r.dtype = MSR_BF16;
+    r.flags |= msr::kFlagNoWide;  // the 64-column chunk kernels are faster for these calls
     return r;
 }
 

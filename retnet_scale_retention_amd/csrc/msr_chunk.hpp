@@ -33,6 +33,12 @@ struct ChunkArgs {
     int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
 };
 
+// Problem flag set only on the library's own sub-problems (the public entry
+// points reject it like any unknown flag): keep the chunk recurrence on the
+// 64-column kernels.  The backward pass sets it on its retention calls, for
+// which those kernels are faster (they need no segment end states).
+constexpr uint32_t kFlagNoWide = 1u << 31;
+
 // The wide-slice chunk kernel (k_chunk_wide.hip): true when it takes this
 // shape (d_k 128 or 256, b = 64, d_v a multiple of 256).
 bool chunk_wide_supported(int dk, int dv, int bc);
