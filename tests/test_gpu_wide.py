@@ -86,3 +86,23 @@ def test_wide_state_out_over_state_in_and_determinism():
     o2, s2b = run(q, k, v, g, 64, s_in=s)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2b)
     assert out_err(o1, ro) < TOL["bf16"] and state_err(s1, rs) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("gamma", [0.5, 0.25])
+def test_wide_split_scores_strong_decay(gamma):
+    """The split-scores option (two-term bf16 q~, k~ in the scores) on the
+    wide-slice kernel: within tolerance at strong decay and no worse than the
+    plain call."""
+    import retnet_scale_retention_amd as msr
+    w = mi.Workload("wide-strong", 44, 1, 512, 2, 256, 512, "bf16", (64,))
+    q, k, v = mi.qkv(w)
+    g = np.full(2, gamma, np.float32)
+    s = mi.state(w, 0.5)
+    ro, rs = orc.chunkwise(q, k, v, g, 64, s_in=s, pos0=9)
+    note(f"wide split scores gamma {gamma}")
+    o1, s1 = run(q, k, v, g, 64, s_in=s, pos0=9)
+    o2, s2 = run(q, k, v, g, 64, s_in=s, pos0=9, flags=msr.MSR_FLAG_SPLIT_SCORES)
+    e1, e2 = out_err(o1, ro), out_err(o2, ro)
+    note(f"  O err {e1:.2e} plain, {e2:.2e} split scores; state err {state_err(s2, rs):.2e}")
+    assert e2 < TOL["bf16"] and state_err(s2, rs) < TOL["bf16"]
+    assert e2 <= e1 * 1.05
