@@ -1203,8 +1203,10 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
 
 // Parallel form (jsqmd.com s4.1; aiqz.cc "parallel representation"):
 //   O[n] = GN( sum_{m<=n} s gamma^(n-m) (q~_n . k~_m) v_m + gamma^(n+1) q~_n S_in )
-// One workgroup of four waves per (pair, block of 64 queries, 64-column
-// value slice); wave w owns query tile 4 qb + w.  Per 32-key block up to the
+// One workgroup of four waves per (pair, block of 64 queries, value slice
+// of PW columns: 256 when d_v allows, else 64); wave w owns query tile
+// 4 qb + w.  The scores are formed once per slice, so the wider slice does
+// them a quarter as often.  Per 32-key block up to the
 // diagonal, the K~ fragments (prep_kernel, PAR) and the V slice stream into
 // double-buffered LDS by direct loads; each wave forms P^T = K~ Q~^T with
 // bf16 MFMA, applies s gamma^(n-m) and the causal mask in registers, and
@@ -1221,22 +1223,30 @@ struct ParArgs {
     int NS;
 };
 
-template <int DK>
+template <int DK, int PW>
 __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs a) {
     using C = Cfg<DK, 64>;
     constexpr int KS = DK / 32;
+    constexpr int CT = PW / 16;            // 16-column tiles of the slice
     constexpr int KBYTES = 2 * KS * 1024;  // K~ fragments of one 32-key block
-    constexpr int VBYTES = 32 * W * 2;     // V slice of one 32-key block
+    constexpr int VBYTES = 32 * PW * 2;    // V slice of one 32-key block
+    constexpr int NVL = VBYTES / 1024 / 4; // 1 KiB direct loads of it per wave
+    static_assert(PW % 64 == 0 && NVL >= 1, "slice width");
+    // V rows (PW 2 bytes) with their 16-byte chunks XOR-swizzled by row so
+    // that the transpose reads of a 16-lane group (4 rows x 32 bytes) spread
+    // over the banks
+    auto vswz = [](int r) { return PW == 64 ? (r >> 1) & 7 : ((r & 3) << 1) | ((r >> 2) & 1); };
+    auto voffp = [&](int r, int col) { return r * (PW * 2) + ((((col >> 3) ^ vswz(r))) << 4) + (col & 7) * 2; };
     __shared__ __attribute__((aligned(16))) char Kb0[KBYTES], Kb1[KBYTES];
     __shared__ __attribute__((aligned(16))) char Vb0[VBYTES], Vb1[VBYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_in^T slice
+    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_in^T, 64 columns at a time
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int nqb = c.T / 64;
     const int slice = blockIdx.x % a.NS, qb = (blockIdx.x / a.NS) % nqb, pair = blockIdx.x / a.NS / nqb;
     const int b = pair / c.H, h = pair % c.H;
-    const int col0 = slice * W;
+    const int col0 = slice * PW;
     const float lg = c.log2g[h];
     const int tile = 4 * qb + w;              // this wave's query tile
     const int n = 16 * tile + l16;            // this lane's query row (as MFMA column)
@@ -1251,9 +1261,12 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     auto dma = [&](int kb, char *kd, char *vd) {
         const char *ks = reinterpret_cast<const char *>(kqb + (size_t)(2 * kb) * KS * FRAG);
         for (int u = w; u < 2 * KS; u += 4) load_lds16(ks + u * 1024 + loff, kd + u * 1024);
-        const int byte = w * 1024 + lane * 16;
-        const int row = byte / (W * 2), phys = (byte % (W * 2)) >> 4;
-        load_lds16(vb + (uint32_t)(32 * kb + row) * rowV + (phys ^ C::swz_v(row)) * 16, vd + w * 1024);
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int unit = 4 * i + w, byte = unit * 1024 + lane * 16;
+            const int row = byte / (PW * 2), phys = (byte % (PW * 2)) >> 4;
+            load_lds16(vb + (uint32_t)(32 * kb + row) * rowV + (phys ^ vswz(row)) * 16, vd + unit * 1024);
+        }
     };
 
     bf16x8 qr[KS];
@@ -1262,25 +1275,30 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
         qr[ks] = *reinterpret_cast<const bf16x8 *>(
             reinterpret_cast<const char *>(qfb + (size_t)(tile * KS + ks) * FRAG) + loff);
 
-    f32x4 oacc[C::CT];
+    f32x4 oacc[CT];
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.s_in) {  // (S_in^T Q~^T) gamma^(n+1)
-        const float *sp = a.s_in + (size_t)pair * DK * c.dv + col0;
-        for (int e = tid; e < DK * W; e += 256) {
-            const int row = e / W, col = e % W;
-            St[col * C::SP + row] = static_cast<__bf16>(sp[(size_t)row * c.dv + col]);
+    for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.s_in) {  // (S_in^T Q~^T) gamma^(n+1), 64 value columns at a time
+#pragma unroll
+        for (int sc = 0; sc < PW / W; ++sc) {
+            const float *sp = a.s_in + (size_t)pair * DK * c.dv + col0 + sc * W;
+            if (sc > 0) __syncthreads();  // every wave is done with the previous columns
+            for (int e = tid; e < DK * W; e += 256) {
+                const int row = e / W, col = e % W;
+                St[col * C::SP + row] = static_cast<__bf16>(sp[(size_t)row * c.dv + col]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < W / 16; ++t)
+                    oacc[sc * (W / 16) + t] = mfma16(
+                        *reinterpret_cast<const bf16x8 *>(St + (t * 16 + l16) * C::SP + 32 * ks + 8 * g), qr[ks],
+                        oacc[sc * (W / 16) + t]);
         }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct)
-                oacc[ct] = mfma16(*reinterpret_cast<const bf16x8 *>(St + (ct * 16 + l16) * C::SP + 32 * ks + 8 * g),
-                                  qr[ks], oacc[ct]);
         const float x = exp2f((float)(n + 1) * lg);
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * x;
+        for (int ct = 0; ct < CT; ++ct) oacc[ct] = oacc[ct] * x;
     }
 
     const int nkb = 2 * qb + 2;  // key blocks up to the block's last query
@@ -1306,10 +1324,10 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
                     static_cast<__bf16>(m <= n ? acc[v2][r] * c.scale * exp2f((float)(n - m) * lg) : 0.f);
             }
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {
             const int col = ct * 16 + 4 * (l16 & 3);
-            const s16x4 v0 = lds_tr(Vc + C::voff(4 * g + (l16 >> 2), col));
-            const s16x4 v1 = lds_tr(Vc + C::voff(16 + 4 * g + (l16 >> 2), col));
+            const s16x4 v0 = lds_tr(Vc + voffp(4 * g + (l16 >> 2), col));
+            const s16x4 v1 = lds_tr(Vc + voffp(16 + 4 * g + (l16 >> 2), col));
             oacc[ct] = mfma16(cat(v0, v1), pb, oacc[ct]);
         }
     };
@@ -1325,32 +1343,32 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
         const float f = 1.f / decay_row_sum(row_pos0(c, b) + n, lg);
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = oacc[ct] * f;
+        for (int ct = 0; ct < CT; ++ct) oacc[ct] = oacc[ct] * f;
     }
     if (norm_here || stats_out) {
         float sum = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) sum += oacc[ct][0] + oacc[ct][1] + oacc[ct][2] + oacc[ct][3];
-        const float mean = sum_lane_groups(sum) * (1.f / W);
+        for (int ct = 0; ct < CT; ++ct) sum += oacc[ct][0] + oacc[ct][1] + oacc[ct][2] + oacc[ct][3];
+        const float mean = sum_lane_groups(sum) * (1.f / PW);
         float m2 = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) m2 += (oacc[ct][r] - mean) * (oacc[ct][r] - mean);
         m2 = sum_lane_groups(m2);
         if (stats_out && g == 0)
             a.stats[((size_t)b * c.T * c.H + rowi) * a.NS + slice] = make_float2(mean, m2);
         if (norm_here) {
-            const float inv = 1.f / sqrtf(m2 * (1.f / W) + c.eps);
+            const float inv = 1.f / sqrtf(m2 * (1.f / PW) + c.eps);
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) oacc[ct][r] = (oacc[ct][r] - mean) * inv;
         }
     }
     uint16_t *dst = a.o + ((size_t)b * c.T * c.H + rowi) * c.dv + col0 + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
         const u32x2 v2 = {pack_bf16x2(oacc[ct][0], oacc[ct][1]), pack_bf16x2(oacc[ct][2], oacc[ct][3])};
         *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
     }
@@ -1554,19 +1572,21 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     const ParPlan m = par_plan(p);
     char *wsb = static_cast<char *>(ws);
     const int npairs = c.B * c.H, nqb = c.T / 64, NS = c.dv / W;
+    const int PW = c.dv % 256 == 0 ? 256 : W;  // value columns per output workgroup
+    const int NSO = c.dv / PW;                  // output slices (and GroupNorm partials) per row
     uint16_t *qf = reinterpret_cast<uint16_t *>(wsb + m.qf), *kq = reinterpret_cast<uint16_t *>(wsb + m.kq);
     uint16_t *kf = reinterpret_cast<uint16_t *>(wsb + m.kf);
-    float2 *stats = NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
+    float2 *stats = NSO > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
     auto pk = prep_kernel<DK, 64, true>;
     hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq, (const uint16_t *)nullptr,
                        (const uint16_t *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NS};
+    ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
     main_kernel_begin(st);
-    auto ok = parallel_mfma_kernel<DK>;
-    hipLaunchKernelGGL(ok, dim3(npairs * nqb * NS), dim3(256), 0, st, c, pa);
+    auto ok = PW == 256 ? parallel_mfma_kernel<DK, 256> : parallel_mfma_kernel<DK, 64>;
+    hipLaunchKernelGGL(ok, dim3(npairs * nqb * NSO), dim3(256), 0, st, c, pa);
     e = hipGetLastError();
     main_kernel_end(st);
     if (e != hipSuccess) return e;
@@ -1591,10 +1611,10 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
         hipLaunchKernelGGL(sk, dim3(npairs * NS), dim3(Cfg<DK, 64>::THREADS), 0, st, c, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+    if (NSO > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;
         const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
-        hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, NS, stats,
+        hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, NSO, stats,
                            static_cast<uint16_t *>(O), rows);
         e = hipGetLastError();
     }

@@ -136,13 +136,16 @@ def test_mfma_segments_vs_oracle(case):
 # The bf16 parallel form (T a multiple of 64) runs its own MFMA kernel: causal
 # score blocks per 64-query block with the decay applied in registers, the
 # incoming-state term from S_in^T, and the outgoing state as one decayed sum.
-PAR_CASES = [  # (B, T, H, dk, dv)
+PAR_CASES = [  # (B, T, H, dk, dv); d_v a multiple of 256 takes 256-column output slices
     (1, 64, 2, 64, 64),
     (2, 192, 2, 64, 128),
     (1, 512, 2, 128, 64),
     (1, 320, 2, 128, 192),
     (1, 256, 2, 256, 64),
     (1, 512, 1, 256, 128),
+    (2, 128, 2, 64, 256),
+    (1, 320, 2, 128, 256),
+    (1, 192, 2, 256, 512),
 ]
 
 
@@ -175,8 +178,9 @@ def test_mfma_parallel_vs_oracle(case):
 
 
 @pytest.mark.parametrize("flags", [1, 2])
-def test_mfma_parallel_flags(flags):
-    w = mi.Workload("mfma-par-flags", 37, 1, 256, 2, 128, 128, "bf16", (256,))
+@pytest.mark.parametrize("dv", [128, 512])
+def test_mfma_parallel_flags(flags, dv):
+    w = mi.Workload("mfma-par-flags", 37, 1, 256, 2, 128, dv, "bf16", (256,))
     q, k, v = mi.qkv(w)
     g = mi.gammas(2)
     ro, rs = orc.parallel(q, k, v, g, rotate=not (flags & 1), groupnorm=not (flags & 2))
