@@ -1237,9 +1237,12 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     // over the banks
     auto vswz = [](int r) { return PW == 64 ? (r >> 1) & 7 : ((r & 3) << 1) | ((r >> 2) & 1); };
     auto voffp = [&](int r, int col) { return r * (PW * 2) + ((((col >> 3) ^ vswz(r))) << 4) + (col & 7) * 2; };
-    __shared__ __attribute__((aligned(16))) char Kb0[KBYTES], Kb1[KBYTES];
-    __shared__ __attribute__((aligned(16))) char Vb0[VBYTES], Vb1[VBYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 St[W * C::SP];  // S_in^T, 64 columns at a time
+    // K~ and V double buffers; before the first block the same LDS holds
+    // S_in^T, 64 columns at a time (so that two workgroups fit on a CU)
+    __shared__ __attribute__((aligned(16))) char L[2 * KBYTES + 2 * VBYTES];
+    static_assert(W * C::SP * 2 <= 2 * KBYTES + 2 * VBYTES, "S_in^T staging fits the K~/V buffers");
+    char *const Kb0 = L, *const Kb1 = L + KBYTES, *const Vb0 = L + 2 * KBYTES, *const Vb1 = L + 2 * KBYTES + VBYTES;
+    __bf16 *const St = reinterpret_cast<__bf16 *>(L);
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
@@ -1299,6 +1302,7 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
         const float x = exp2f((float)(n + 1) * lg);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) oacc[ct] = oacc[ct] * x;
+        __syncthreads();  // every wave is done with S_in^T before the loads overwrite it
     }
 
     const int nkb = 2 * qb + 2;  // key blocks up to the block's last query
