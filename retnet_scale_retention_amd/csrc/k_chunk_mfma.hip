@@ -1474,7 +1474,7 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, bool wide, const 
                         const void *Qlo, const void *Klo, hipStream_t st) {
     using C = Cfg<DK, BC>;
     hipError_t e = hipSuccess;
-    if constexpr (C::QSTAGE && BC == 64 && DK >= 128) {
+    if constexpr (C::QSTAGE && BC <= 128 && DK >= 128) {
         if (wide) {  // 256-column slices (k_chunk_wide.hip)
             launch_prep<DK, BC, true>(c, a, Q, K, Qlo, Klo, st);
             if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1545,7 +1545,14 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
     m.pf = m.kf + up(tokens * p->dk * 2);
     // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
     m.stats = m.pf + up(tokens * chunk * 2);
-    m.wide = chunk_wide_supported(p->dk, p->dv, chunk) && !(p->flags & kFlagNoWide);
+    // The wide-slice kernel at b = 64, where it is the faster one even with
+    // its state-only segment pass (7B-shaped layer: 0.53 against about
+    // 0.73 ms per call), and at b = 128 when it needs no segments (one
+    // workgroup per (pair, 256 columns) already fills the GPU): its full
+    // pass is faster than the warp-specialised kernel's (253 against 303 us
+    // at the 7B shape), but not by the 89 us its segment pass costs there.
+    const bool wide_ok = chunk_wide_supported(p->dk, p->dv, chunk) && !(p->flags & kFlagNoWide);
+    m.wide = wide_ok && (chunk == 64 || choose_nseg(p, chunk, 256) == 1);
     m.NS = p->dv / (m.wide ? 32 : W);  // GroupNorm partials per row
     m.segE = m.stats + (m.NS > 1 ? up(tokens * m.NS * sizeof(float2)) : 0);
     m.nseg = choose_nseg(p, chunk, m.wide ? 256 : W);

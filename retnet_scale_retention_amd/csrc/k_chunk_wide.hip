@@ -609,20 +609,18 @@ hipError_t launch_wide(const MsrConst &c, const ChunkArgs &a, bool so, hipStream
 
 namespace msr {
 
-// Taken at b = 64, where it is faster than the 64-column kernels (7B-shaped
-// layer: 565 against about 730 us per call).  At b = 128 the 64-column
-// warp-specialised kernel, which needs no segments at that shape, stays
-// ahead (about 570 against 646 us), so the wide kernel is not used there.
 bool chunk_wide_supported(int dk, int dv, int bc) {
-    return (dk == 128 || dk == 256) && bc == 64 && dv % WS == 0;
+    return (dk == 128 || dk == 256) && (bc == 64 || bc == 128) && dv % WS == 0;
 }
 
 hipError_t launch_chunk_wide(const MsrConst &c, const ChunkArgs &a, int bc, bool state_only, hipStream_t st) {
     if (!chunk_wide_supported(c.dk, c.dv, bc) || a.NW2 != c.dv / WS) return hipErrorInvalidValue;
     if (state_only && (a.nseg < 2 || !a.segE)) return hipErrorInvalidValue;
-    switch (c.dk) {
-    case 128: return launch_wide<128, 64>(c, a, state_only, st);
-    case 256: return launch_wide<256, 64>(c, a, state_only, st);
+    switch (c.dk * 1000 + bc) {
+    case 128064: return launch_wide<128, 64>(c, a, state_only, st);
+    case 128128: return launch_wide<128, 128>(c, a, state_only, st);
+    case 256064: return launch_wide<256, 64>(c, a, state_only, st);
+    case 256128: return launch_wide<256, 128>(c, a, state_only, st);
     default: return hipErrorNotSupported;
     }
 }

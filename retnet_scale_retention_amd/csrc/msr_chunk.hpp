@@ -39,8 +39,8 @@ struct ChunkArgs {
 // which those kernels are faster (they need no segment end states).
 constexpr uint32_t kFlagNoWide = 1u << 31;
 
-// The wide-slice chunk kernel (k_chunk_wide.hip): true when it takes this
-// shape (d_k 128 or 256, b = 64, d_v a multiple of 256).
+// The wide-slice chunk kernel (k_chunk_wide.hip): true when it can take
+// this shape (d_k 128 or 256, b 64 or 128, d_v a multiple of 256).
 bool chunk_wide_supported(int dk, int dv, int bc);
 
 // Launches the wide-slice chunk kernel over pairs x a.NW2 x a.nseg

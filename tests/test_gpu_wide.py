@@ -1,5 +1,6 @@
 """GPU parity of the wide-slice chunk kernel (a workgroup per 256 value
-columns; taken for d_k 128 or 256, chunk 64 and d_v a multiple of 256)
+columns; taken for d_k 128 or 256 and d_v a multiple of 256, at chunk 64, and at
+chunk 128 when no segments are needed)
 against the fp64 oracle: one segment and several, an incoming state, a
 non-zero start position, gammas that rescale the carried state every chunk
 or never, the flags, an outgoing state written over the incoming one, and
@@ -106,3 +107,26 @@ def test_wide_split_scores_strong_decay(gamma):
     note(f"  O err {e1:.2e} plain, {e2:.2e} split scores; state err {state_err(s2, rs):.2e}")
     assert e2 < TOL["bf16"] and state_err(s2, rs) < TOL["bf16"]
     assert e2 <= e1 * 1.05
+
+
+# b = 128 takes the wide-slice kernel when one workgroup per (pair, 256
+# columns) already fills the GPU, i.e. with no segments
+CASES_128 = [  # (B, T, H, dk, dv, chunk)
+    (8, 256, 16, 256, 256, 128),
+    (4, 384, 32, 128, 256, 128),
+]
+
+
+@pytest.mark.parametrize("case", CASES_128, ids=lambda c: "B%dT%dH%ddk%ddv%db%d" % c)
+def test_wide_b128_vs_oracle(case):
+    B, T, H, dk, dv, b = case
+    w = mi.Workload("wide128", 45, B, T, H, dk, dv, "bf16", (b,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = np.resize(GAMMAS, H).astype(np.float32)
+    note(f"wide b=128 {case}: oracle")
+    ro, rs = orc.recurrent(q, k, v, g, s_in=s, pos0=5)
+    o, st = run(q, k, v, g, b, s_in=s, pos0=5)
+    eo, es = out_err(o, ro), state_err(st, rs)
+    note(f"  O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
