@@ -95,10 +95,11 @@ __global__ void rotate_tok_kernel(MsrConst c, const TIn *__restrict__ x, TOut *_
 }
 
 // The same, four pairs (8 elements, one or two 16-byte accesses) per work
-// item; d_k a multiple of 8
+// item; d_k a multiple of 8.  rev: output token t reads input token T-1-t of
+// its batch row (the rotation still takes the output's position).
 template <typename TIn, typename TOut>
 __global__ void rotate_tok8_kernel(MsrConst c, const TIn *__restrict__ x, TOut *__restrict__ y,
-                                   TOut *__restrict__ ylo, float factor, float sign) {
+                                   TOut *__restrict__ ylo, float factor, float sign, int rev) {
     const int g8 = c.dk / 8;
     const size_t n = (size_t)c.B * c.T * c.H * g8;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
@@ -106,7 +107,8 @@ __global__ void rotate_tok8_kernel(MsrConst c, const TIn *__restrict__ x, TOut *
         const size_t r = e / g8;           // (b T + t) H + h
         const int t = (int)((r / c.H) % c.T), b = (int)(r / ((size_t)c.H * c.T));
         float v[8], hi[8], lo[8];
-        ldv<8>(x + 8 * e, v);
+        const size_t rx = rev ? ((size_t)b * c.T + (c.T - 1 - t)) * c.H + r % c.H : r;
+        ldv<8>(x + 8 * (rx * g8 + e % g8), v);
         const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
         const int64_t pos = rot ? row_pos0(c, b) + t : 0;
 #pragma unroll
@@ -312,17 +314,18 @@ hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream
 
 template <typename TIn>
 hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, int out_dtype, float factor,
-                         float sign, hipStream_t st) {
+                         float sign, int rev, hipStream_t st) {
     const size_t n = (size_t)c.B * c.T * c.H * (c.dk / 2);
     if (n == 0) return hipSuccess;
+    if (rev && c.dk % 8 != 0) return hipErrorNotSupported;
     if (c.dk % 8 == 0) {
         const size_t n8 = n / 4;
         if (out_dtype == MSR_BF16)
             hipLaunchKernelGGL((rotate_tok8_kernel<TIn, uint16_t>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
-                               static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign);
+                               static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign, rev);
         else
             hipLaunchKernelGGL((rotate_tok8_kernel<TIn, float>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
-                               static_cast<float *>(y), nullptr, factor, sign);
+                               static_cast<float *>(y), nullptr, factor, sign, rev);
         return hipGetLastError();
     }
     if (out_dtype == MSR_BF16)
@@ -335,11 +338,11 @@ hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, in
 }
 
 hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
-                             float sign, hipStream_t st, void *ylo) {
+                             float sign, hipStream_t st, void *ylo, int rev) {
     if (ylo && out_dtype != MSR_BF16) return hipErrorInvalidValue;
     if (in_dtype == MSR_BF16)
-        return rotate_tok_in(c, static_cast<const uint16_t *>(x), y, ylo, out_dtype, factor, sign, st);
-    return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, st);
+        return rotate_tok_in(c, static_cast<const uint16_t *>(x), y, ylo, out_dtype, factor, sign, rev, st);
+    return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, rev, st);
 }
 
 template <int PER, typename TX, typename TIn>

@@ -265,8 +265,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
             zet[t] = c.scale * exp2f((float)(BC - 1 - t - BC * (ci % rescale_period(lg, BC))) * lg);
     }
 
-    const uint32_t rowQK = (uint32_t)c.H * DK * 2;  // bytes between tokens of Q, K
-    const size_t base = (((size_t)b * c.T + (size_t)ci * BC) * c.H + h) * DK;
+    const int ld = c.ldqk ? c.ldqk : DK;            // Q, K may be column slices of wider rows
+    const uint32_t rowQK = (uint32_t)c.H * ld * 2;  // bytes between tokens of Q, K
+    const size_t base = (((size_t)b * c.T + (size_t)ci * BC) * c.H + h) * ld;
     const char *qrow = reinterpret_cast<const char *>(q + base);
     const char *krow = reinterpret_cast<const char *>(k + base);
 

@@ -17,7 +17,8 @@ struct MsrConst {
     float scale;       // multiplies the rotated K
     float eps;         // GroupNorm epsilon
     uint32_t flags;    // MSR_FLAG_*
-    int32_t pad_;
+    int32_t ldqk;      // elements between (token, head) rows of the Q and K the
+                       // MFMA prep kernel reads (0: d_k, i.e. packed rows)
     float gamma[MSR_MAX_HEADS];   // decay per head
     float log2g[MSR_MAX_HEADS];   // log2(gamma), computed in fp64 on the host
     float theta[MSR_MAX_DK / 2];  // rotation frequency per channel pair
@@ -58,9 +59,10 @@ hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out,
 // (every x / y below is an MSR_F32 or MSR_BF16 array as its *_dtype says)
 hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream_t st);
 // y = factor * R(sign * angle) x on token-major [B][T][H][dk] rows; with ylo
-// (bf16 output only) y + ylo is a two-term bf16 split of the fp32 result
+// (bf16 output only) y + ylo is a two-term bf16 split of the fp32 result;
+// rev: row t of y comes from row T-1-t of x (d_k a multiple of 8 only)
 hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
-                             float sign, hipStream_t st, void *ylo = nullptr);
+                             float sign, hipStream_t st, void *ylo = nullptr, int rev = 0);
 // GroupNorm backward per row of dv values: x = GroupNorm's input, dy = dL/d(output) -> dx
 hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int x_dtype, const void *dy,
                               int dy_dtype, void *dx, int out_dtype, hipStream_t st);
