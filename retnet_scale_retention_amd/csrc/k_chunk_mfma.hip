@@ -267,7 +267,11 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
 
     const int ld = c.ldqk ? c.ldqk : DK;            // Q, K may be column slices of wider rows
     const uint32_t rowQK = (uint32_t)c.H * ld * 2;  // bytes between tokens of Q, K
-    const size_t base = (((size_t)b * c.T + (size_t)ci * BC) * c.H + h) * ld;
+    const bool rv = c.revqk != 0;
+    const int tlo = rv ? c.T - (ci + 1) * BC : ci * BC;  // lowest source token of the chunk
+    const size_t base = (((size_t)b * c.T + (size_t)tlo) * c.H + h) * ld;
+    // byte offset of the chunk's row r from base
+    auto roff = [&](int r) { return (uint32_t)(rv ? BC - 1 - r : r) * rowQK; };
     const char *qrow = reinterpret_cast<const char *>(q + base);
     const char *krow = reinterpret_cast<const char *>(k + base);
 
@@ -277,8 +281,8 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
         u32x4 xq[RPT], xk[RPT];
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
-            xq[j] = ld16(qrow, (uint32_t)(r0 + j) * rowQK + c8 * 16);
-            xk[j] = ld16(krow, (uint32_t)(r0 + j) * rowQK + c8 * 16);
+            xq[j] = ld16(qrow, roff(r0 + j) + c8 * 16);
+            xk[j] = ld16(krow, roff(r0 + j) + c8 * 16);
         }
         float cc[4] = {1.f, 1.f, 1.f, 1.f}, ss[4] = {0.f, 0.f, 0.f, 0.f}, c1[4], s1[4];
         const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
@@ -412,11 +416,11 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
                 bf16x8 kla[2], qlb[NU];
 #pragma unroll
                 for (int v2 = 0; v2 < 2; ++v2)
-                    kla[v2] = __builtin_bit_cast(bf16x8, ld16(kl, (uint32_t)(32 * kb + 16 * v2 + l16) * rowQK +
+                    kla[v2] = __builtin_bit_cast(bf16x8, ld16(kl, roff(32 * kb + 16 * v2 + l16) +
                                                                       (32 * ks + 8 * g) * 2));
 #pragma unroll
                 for (int u = 0; u < NU; ++u)
-                    qlb[u] = __builtin_bit_cast(bf16x8, ld16(ql, (uint32_t)(16 * qt[u] + l16) * rowQK +
+                    qlb[u] = __builtin_bit_cast(bf16x8, ld16(ql, roff(16 * qt[u] + l16) +
                                                                  (32 * ks + 8 * g) * 2));
 #pragma unroll
                 for (int u = 0; u < NU; ++u)

@@ -256,7 +256,7 @@ bool mfma_backward_ok(const msr_problem *p, int chunk) {
 }
 
 struct BackPlanM {
-    size_t oraw = 0, g = 0, qr = 0, kr = 0, ql = 0, kl = 0, qrrev = 0, krrev = 0, qlrev = 0, klrev = 0, grev = 0,
+    size_t oraw = 0, g = 0, qr = 0, kr = 0, ql = 0, kl = 0, qrrev = 0, grev = 0,
            part = 0, acc = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, mws = 0, total = 0;
 };
 
@@ -276,9 +276,6 @@ BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
     b.ql = take(N * dk * 2);
     b.kl = take(N * dk * 2);
     b.qrrev = take(N * dk * 2);
-    b.krrev = take(N * dk * 2);
-    b.qlrev = take(N * dk * 2);
-    b.klrev = take(N * dk * 2);
     b.grev = take(N * dv * 2);
     b.part = take(N * dk * 2);
     b.acc = take(N * dk * 4);
@@ -303,12 +300,14 @@ BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
 // One retention call on the MFMA path (no rotation, no GroupNorm, scale 1).
 // (Qlo, Klo: low parts of two-term bf16 splits of Q and K for the scores;
 // ldqk: elements between rows of Q and K when they are column slices of
-// wider rows, 0 for packed rows)
+// wider rows, 0 for packed rows; revqk: Q, K (and Qlo, Klo) are read in
+// reverse time order, V is taken as given)
 hipError_t mfma_ret(const msr_problem *sub, int chunk, const void *Q, const void *K, const void *V, void *O,
                     const float *s_in, float *s_out, void *ws, hipStream_t st, const void *Qlo = nullptr,
-                    const void *Klo = nullptr, int ldqk = 0) {
+                    const void *Klo = nullptr, int ldqk = 0, int revqk = 0) {
     MsrConst c = make_const(sub, chunk);
     c.ldqk = ldqk;
+    c.revqk = revqk;
     return mfma_chunkwise(c, sub, chunk, Q, K, V, O, s_in, s_out, ws, st, Qlo, Klo);
 }
 
@@ -365,29 +364,26 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     }
     ok(launch_rotate_tok(c, F(b.acc), MSR_F32, dQ, BF, 1.f, -1.f, st));
     // 4. dk~ (backward in time) = sum over parts of Ret(V_part, G_part, Q~; dS_out^T / gamma rows);
-    //    V reversed in time goes where the pre-norm outputs were (no longer
-    //    needed), G reversed is kept for 5.
+    //    the prep kernel reads V_part and G_part in reverse time order in
+    //    place, the value operand Q~ is a reversed copy
     ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.qr), BF, P(b.qrrev), BF, st));
-    ok(launch_slice(B, T, H, dv, 0, dv, 1, V, BF, P(b.oraw), BF, st));
-    ok(launch_slice(B, T, H, dv, 0, dv, 1, g, BF, P(b.grev), BF, st));
     for (int i = 0; i < np && e == hipSuccess; ++i) {
         const msr_problem a = mfma_sub(p, len[i], dk);
         float *dsoT = dstate_out ? F(b.s2) : nullptr;
         if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, off[i], len[i], st));
-        ok(mfma_ret(&a, chunk, col(P(b.oraw), off[i]), col(P(b.grev), off[i]), P(b.qrrev), P(b.part), dsoT,
-                    nullptr, P(b.mws), st, nullptr, nullptr, dv));
+        ok(mfma_ret(&a, chunk, col(V, off[i]), col(g, off[i]), P(b.qrrev), P(b.part), dsoT, nullptr, P(b.mws), st,
+                    nullptr, nullptr, dv, 1));
         ok(launch_accumulate(N * dk, P(b.part), BF, F(b.acc), i == 0, st));
     }
     ok(launch_rotate_tok(c, F(b.acc), MSR_F32, dK, BF, c.scale, -1.f, st, nullptr, 1));
     // 5. dV (backward in time) = Ret(K~, Q~, G; dS_out / gamma), its scores
     //    split as in 1.; its outgoing state times gamma is dS_in
-    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kr), BF, P(b.krrev), BF, st));
-    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.kl), BF, P(b.klrev), BF, st));
-    ok(launch_slice(B, T, H, dk, 0, dk, 1, P(b.ql), BF, P(b.qlrev), BF, st));
+    //    (K~, Q~ and their low parts read reversed in place, G as a reversed copy)
+    ok(launch_slice(B, T, H, dv, 0, dv, 1, g, BF, P(b.grev), BF, st));
     float *dso = dstate_out ? F(b.s3) : nullptr, *sc = dstate_in ? F(b.s4) : nullptr;
     if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dso, 0, -1.f, 0, dv, st));
-    ok(mfma_ret(&pc, chunk, P(b.krrev), P(b.qrrev), P(b.grev), P(b.oraw), dso, sc, P(b.mws), st, P(b.klrev),
-                P(b.qlrev)));
+    ok(mfma_ret(&pc, chunk, P(b.kr), P(b.qr), P(b.grev), P(b.oraw), dso, sc, P(b.mws), st, P(b.kl), P(b.ql), 0,
+                1));
     ok(launch_slice(B, T, H, dv, 0, dv, 1, P(b.oraw), BF, dV, BF, st));
     if (dstate_in) ok(launch_state_op(c, dk, dv, sc, dstate_in, 0, 1.f, 0, dv, st));
     return e;

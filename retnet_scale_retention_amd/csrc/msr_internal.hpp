@@ -19,6 +19,8 @@ struct MsrConst {
     uint32_t flags;    // MSR_FLAG_*
     int32_t ldqk;      // elements between (token, head) rows of the Q and K the
                        // MFMA prep kernel reads (0: d_k, i.e. packed rows)
+    int32_t revqk;     // nonzero: that kernel takes Q and K in reverse time order
+                       // (token t of a batch row reads token T-1-t)
     float gamma[MSR_MAX_HEADS];   // decay per head
     float log2g[MSR_MAX_HEADS];   // log2(gamma), computed in fp64 on the host
     float theta[MSR_MAX_DK / 2];  // rotation frequency per channel pair
