@@ -96,10 +96,12 @@ __global__ void rotate_tok_kernel(MsrConst c, const TIn *__restrict__ x, TOut *_
 
 // The same, four pairs (8 elements, one or two 16-byte accesses) per work
 // item; d_k a multiple of 8.  rev: output token t reads input token T-1-t of
-// its batch row (the rotation still takes the output's position).
+// its batch row (the rotation still takes the output's position).  x2 (bf16,
+// optional, same layout as x) is added to x before the rotation.
 template <typename TIn, typename TOut>
 __global__ void rotate_tok8_kernel(MsrConst c, const TIn *__restrict__ x, TOut *__restrict__ y,
-                                   TOut *__restrict__ ylo, float factor, float sign, int rev) {
+                                   TOut *__restrict__ ylo, float factor, float sign, int rev,
+                                   const uint16_t *__restrict__ x2) {
     const int g8 = c.dk / 8;
     const size_t n = (size_t)c.B * c.T * c.H * g8;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
@@ -109,6 +111,12 @@ __global__ void rotate_tok8_kernel(MsrConst c, const TIn *__restrict__ x, TOut *
         float v[8], hi[8], lo[8];
         const size_t rx = rev ? ((size_t)b * c.T + (c.T - 1 - t)) * c.H + r % c.H : r;
         ldv<8>(x + 8 * (rx * g8 + e % g8), v);
+        if (x2) {
+            float v2[8];
+            ldv<8>(x2 + 8 * (rx * g8 + e % g8), v2);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] += v2[j];
+        }
         const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
         const int64_t pos = rot ? row_pos0(c, b) + t : 0;
 #pragma unroll
@@ -314,18 +322,18 @@ hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream
 
 template <typename TIn>
 hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, int out_dtype, float factor,
-                         float sign, int rev, hipStream_t st) {
+                         float sign, int rev, const uint16_t *x2, hipStream_t st) {
     const size_t n = (size_t)c.B * c.T * c.H * (c.dk / 2);
     if (n == 0) return hipSuccess;
-    if (rev && c.dk % 8 != 0) return hipErrorNotSupported;
+    if ((rev || x2) && c.dk % 8 != 0) return hipErrorNotSupported;
     if (c.dk % 8 == 0) {
         const size_t n8 = n / 4;
         if (out_dtype == MSR_BF16)
             hipLaunchKernelGGL((rotate_tok8_kernel<TIn, uint16_t>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
-                               static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign, rev);
+                               static_cast<uint16_t *>(y), static_cast<uint16_t *>(ylo), factor, sign, rev, x2);
         else
             hipLaunchKernelGGL((rotate_tok8_kernel<TIn, float>), dim3(grid_for(n8)), dim3(256), 0, st, c, x,
-                               static_cast<float *>(y), nullptr, factor, sign, rev);
+                               static_cast<float *>(y), nullptr, factor, sign, rev, x2);
         return hipGetLastError();
     }
     if (out_dtype == MSR_BF16)
@@ -338,11 +346,12 @@ hipError_t rotate_tok_in(const MsrConst &c, const TIn *x, void *y, void *ylo, in
 }
 
 hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
-                             float sign, hipStream_t st, void *ylo, int rev) {
+                             float sign, hipStream_t st, void *ylo, int rev, const void *x2) {
     if (ylo && out_dtype != MSR_BF16) return hipErrorInvalidValue;
+    const uint16_t *a2 = static_cast<const uint16_t *>(x2);
     if (in_dtype == MSR_BF16)
-        return rotate_tok_in(c, static_cast<const uint16_t *>(x), y, ylo, out_dtype, factor, sign, rev, st);
-    return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, rev, st);
+        return rotate_tok_in(c, static_cast<const uint16_t *>(x), y, ylo, out_dtype, factor, sign, rev, a2, st);
+    return rotate_tok_in(c, static_cast<const float *>(x), y, ylo, out_dtype, factor, sign, rev, a2, st);
 }
 
 template <int PER, typename TX, typename TIn>

@@ -257,7 +257,7 @@ bool mfma_backward_ok(const msr_problem *p, int chunk) {
 
 struct BackPlanM {
     size_t oraw = 0, g = 0, qr = 0, kr = 0, ql = 0, kl = 0, qrrev = 0, grev = 0,
-           part = 0, acc = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, mws = 0, total = 0;
+           part = 0, part2 = 0, acc = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, mws = 0, total = 0;
 };
 
 BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
@@ -278,7 +278,9 @@ BackPlanM back_plan_mfma(const msr_problem *p, int chunk) {
     b.qrrev = take(N * dk * 2);
     b.grev = take(N * dv * 2);
     b.part = take(N * dk * 2);
-    b.acc = take(N * dk * 4);
+    b.part2 = take(N * dk * 2);
+    int poff[kMaxParts], plen[kMaxParts];
+    b.acc = take(dv_parts(p->dv, poff, plen) > 2 ? N * dk * 4 : 0);  // fp32 sum of the parts beyond two
     const size_t sp = (size_t)p->B * p->H * 256 * dk * 4, sf = (size_t)p->B * p->H * dk * dv * 4;
     b.s1 = take(sp);
     b.s2 = take(sp);
@@ -354,15 +356,22 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
     // 3. dq~ = sum over the d_v parts of Ret(G_part, V_part, K~; S_in^T rows of the part);
     //    the parts are read in place as column slices (row stride d_v)
     auto col = [](const void *x, int c0) { return static_cast<const void *>(static_cast<const uint16_t *>(x) + c0); };
+    //    The parts' results (bf16) are summed inside the inverse rotation:
+    //    the last part from b.part, the others from b.part2 (two parts) or
+    //    accumulated in fp32 in b.acc (more than two).
+    auto part_out = [&](int i) { return P(i == np - 1 ? b.part : b.part2); };
+    const void *part_sum = np == 1 ? P(b.part) : np == 2 ? P(b.part2) : P(b.acc);
+    const int sum_dtype = np > 2 ? MSR_F32 : BF;
+    const void *part_last = np > 1 ? P(b.part) : nullptr;
     for (int i = 0; i < np && e == hipSuccess; ++i) {
         const msr_problem a = mfma_sub(p, len[i], dk);
         float *sinT = state_in ? F(b.s1) : nullptr;
         if (state_in) ok(launch_state_op(c, dk, dv, state_in, sinT, 1, 0.f, off[i], len[i], st));
-        ok(mfma_ret(&a, chunk, col(g, off[i]), col(V, off[i]), P(b.kr), P(b.part), sinT, nullptr, P(b.mws), st,
+        ok(mfma_ret(&a, chunk, col(g, off[i]), col(V, off[i]), P(b.kr), part_out(i), sinT, nullptr, P(b.mws), st,
                     nullptr, nullptr, dv));
-        ok(launch_accumulate(N * dk, P(b.part), BF, F(b.acc), i == 0, st));
+        if (np > 2 && i < np - 1) ok(launch_accumulate(N * dk, P(b.part2), BF, F(b.acc), i == 0, st));
     }
-    ok(launch_rotate_tok(c, F(b.acc), MSR_F32, dQ, BF, 1.f, -1.f, st));
+    ok(launch_rotate_tok(c, part_sum, sum_dtype, dQ, BF, 1.f, -1.f, st, nullptr, 0, part_last));
     // 4. dk~ (backward in time) = sum over parts of Ret(V_part, G_part, Q~; dS_out^T / gamma rows);
     //    the prep kernel reads V_part and G_part in reverse time order in
     //    place, the value operand Q~ is a reversed copy
@@ -371,11 +380,11 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
         const msr_problem a = mfma_sub(p, len[i], dk);
         float *dsoT = dstate_out ? F(b.s2) : nullptr;
         if (dstate_out) ok(launch_state_op(c, dk, dv, dstate_out, dsoT, 1, -1.f, off[i], len[i], st));
-        ok(mfma_ret(&a, chunk, col(V, off[i]), col(g, off[i]), P(b.qrrev), P(b.part), dsoT, nullptr, P(b.mws), st,
-                    nullptr, nullptr, dv, 1));
-        ok(launch_accumulate(N * dk, P(b.part), BF, F(b.acc), i == 0, st));
+        ok(mfma_ret(&a, chunk, col(V, off[i]), col(g, off[i]), P(b.qrrev), part_out(i), dsoT, nullptr, P(b.mws),
+                    st, nullptr, nullptr, dv, 1));
+        if (np > 2 && i < np - 1) ok(launch_accumulate(N * dk, P(b.part2), BF, F(b.acc), i == 0, st));
     }
-    ok(launch_rotate_tok(c, F(b.acc), MSR_F32, dK, BF, c.scale, -1.f, st, nullptr, 1));
+    ok(launch_rotate_tok(c, part_sum, sum_dtype, dK, BF, c.scale, -1.f, st, nullptr, 1, part_last));
     // 5. dV (backward in time) = Ret(K~, Q~, G; dS_out / gamma), its scores
     //    split as in 1.; its outgoing state times gamma is dS_in
     //    (K~, Q~ and their low parts read reversed in place, G as a reversed copy)

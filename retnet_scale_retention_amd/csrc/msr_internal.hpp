@@ -62,9 +62,11 @@ hipError_t launch_copy_state(const MsrConst &c, const float *s_in, float *s_out,
 hipError_t launch_to_f32(int dtype, size_t n, const void *x, float *y, hipStream_t st);
 // y = factor * R(sign * angle) x on token-major [B][T][H][dk] rows; with ylo
 // (bf16 output only) y + ylo is a two-term bf16 split of the fp32 result;
-// rev: row t of y comes from row T-1-t of x (d_k a multiple of 8 only)
+// rev: row t of y comes from row T-1-t of x; x2 (bf16, x's layout) is added
+// to x first (both: d_k a multiple of 8 only)
 hipError_t launch_rotate_tok(const MsrConst &c, const void *x, int in_dtype, void *y, int out_dtype, float factor,
-                             float sign, hipStream_t st, void *ylo = nullptr, int rev = 0);
+                             float sign, hipStream_t st, void *ylo = nullptr, int rev = 0,
+                             const void *x2 = nullptr);
 // GroupNorm backward per row of dv values: x = GroupNorm's input, dy = dL/d(output) -> dx
 hipError_t launch_gn_backward(size_t rows, int dv, float eps, const void *x, int x_dtype, const void *dy,
                               int dy_dtype, void *dx, int out_dtype, hipStream_t st);

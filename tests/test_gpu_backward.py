@@ -21,6 +21,7 @@ CASES = [
     ("bf16-dk128", 1, 128, 2, 128, 64, "bf16", 128),
     ("bf16-dv512", 1, 256, 2, 64, 512, "bf16", 64),    # d_v in two parts of 256 on the MFMA path
     ("bf16-dv320", 1, 128, 1, 128, 320, "bf16", 64),   # parts 256 + 64
+    ("bf16-dv448", 1, 128, 2, 64, 448, "bf16", 64),    # three parts: 256 + 128 + 64
     ("bf16-T200", 1, 200, 2, 64, 128, "bf16", 64),     # b not dividing T: general path
 ]
 
