@@ -65,8 +65,9 @@
 extern "C" {
 #endif
 
-/* 3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection, msr_qkv_chunkwise (2: pos_rows) */
-#define MSR_ABI_VERSION 3
+/* 4: msr_workspace_bytes; strong-decay routing (3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection,
+ * msr_qkv_chunkwise; 2: pos_rows) */
+#define MSR_ABI_VERSION 4
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
 #define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
 #define MSR_MAX_DV 1024   /* d_v limit */
@@ -102,8 +103,10 @@ typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
  * rotated Q and K (hi.hi + lo.hi + hi.lo) instead of their bf16 roundings.
  * A score much smaller than |q~||k~| otherwise loses its relative accuracy,
  * which GroupNorm amplifies on rows dominated by few tokens -- under strong
- * decay (gamma of about 0.5 or less) enough to reach the bf16 tolerance.
- * Costs a rotation pass and three score products instead of one.
+ * decay enough to reach the bf16 tolerance.  Calls in which any head has
+ * gamma < 0.9 take this route without the flag, msr_parallel included (it
+ * then runs as the equal chunkwise form with chunk 64, 128 or 256).  Costs a
+ * rotation pass and three score products instead of one.
  */
 enum {
     MSR_FLAG_NO_ROTATE = 1u,
@@ -152,6 +155,14 @@ const char *msr_last_error(void);
  */
 msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
                               size_t *bytes);
+
+/*
+ * The same figure as a return value: the workspace bytes `form` needs for p
+ * (chunk as above).  Returns 0 both when no workspace is needed and when p
+ * is invalid; in the second case msr_last_error() says why (so a caller that
+ * must tell the two apart uses msr_workspace_size).
+ */
+size_t msr_workspace_bytes(const msr_problem *p, int32_t form, int32_t chunk);
 
 /*
  * Parallel form over all T tokens of every (batch, head) pair

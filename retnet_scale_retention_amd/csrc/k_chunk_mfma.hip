@@ -453,7 +453,8 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
 // Segments.  When the (pair, slice) workgroups are too few to fill the GPU,
 // each pair's chunks are split into nseg segments of seglen chunks.  The
 // state-only instantiation (SO) runs segments 0 .. nseg-2 from a zero state
-// with only the state update and writes each end state E_g; the full
+// with only the state update and writes each end state E_g (and sets s_in
+// aside in the unused slot of segment nseg-1); the full
 // instantiation then starts segment g from
 //   S_in(g) = gamma^(b seglen) S_in(g-1) + E_(g-1),  S_in(0) = s_in
 // (the chunkwise recurrence regrouped by segments) and writes its outputs.
@@ -489,10 +490,21 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         pair = ps / a.nseg;
         seg = ps % a.nseg;
     }
-    if (SO && !a.par && seg == a.nseg - 1) return;  // the last segment's end state is not needed
+    const int col0 = slice * W;
+    if (SO && !a.par && seg == a.nseg - 1) {
+        // The last segment's end state is not needed.  Its slot holds a copy
+        // of this slice of s_in instead, which the full pass reads: the full
+        // pass may then write s_out over s_in in any workgroup order.
+        const size_t sb = (size_t)pair * DK * c.dv + col0;
+        float *dst = a.segE + (size_t)pair * a.nseg * DK * c.dv + (size_t)seg * DK * c.dv + col0;
+        for (int i = tid; i < DK * W; i += C::THREADS) {
+            const size_t o = (size_t)(i / W) * c.dv + i % W;
+            dst[o] = a.s_in ? a.s_in[sb + o] : 0.f;
+        }
+        return;
+    }
     const int i0 = seg * a.seglen, i1 = i0 + a.seglen;  // this workgroup's chunks
     const int b = pair / c.H, h = pair % c.H;
-    const int col0 = slice * W;
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += C::THREADS) xi[t] = exp2f((float)(t + 1) * lg);
     // (the parallel form's KF fragments carry the whole decay: no rescaling)
@@ -563,6 +575,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     const size_t sbase = (size_t)pair * DK * c.dv + col0;
     // E_g of this pair: segE + ((pair nseg + g) DK + row) dv + col0 + col
     const size_t ebase = (size_t)pair * a.nseg * DK * c.dv + col0;
+    // the incoming state: with segments, the copy the state-only pass made
+    const float *sin_p = a.nseg > 1 ? a.segE + ebase + (size_t)(a.nseg - 1) * DK * c.dv
+                                    : (a.s_in ? a.s_in + sbase : nullptr);
     {
         const float gseg = exp2f((float)(BC * a.seglen) * lg);  // gamma^(b seglen)
         const float f0 = exp2f(-(float)(BC * ph) * lg);         // to the carried scale
@@ -575,7 +590,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                     const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
                     float x = 0.f;
                     if (!SO) {
-                        x = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
+                        x = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
                         for (int gg = 0; gg < seg; ++gg)
                             x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
                         x *= f0;
@@ -958,6 +973,9 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         f32x4 S[C::RPW][C::CPW];
         const size_t sbase = (size_t)pair * DK * c.dv + col0;
         const size_t ebase = (size_t)pair * a.nseg * DK * c.dv + col0;
+        // the incoming state: with segments, the copy the state-only pass made
+        const float *sin_p = a.nseg > 1 ? a.segE + ebase + (size_t)(a.nseg - 1) * DK * c.dv
+                                        : (a.s_in ? a.s_in + sbase : nullptr);
         {
             const float gseg = exp2f((float)(BC * a.seglen) * lg);
             const float f0 = exp2f(-(float)(BC * ph) * lg);
@@ -968,7 +986,7 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                        float x = a.s_in ? a.s_in[sbase + (size_t)row * c.dv + col] : 0.f;
+                        float x = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
                         for (int gg = 0; gg < seg; ++gg)
                             x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
                         S[rt][ct][r] = x * f0;

@@ -400,9 +400,35 @@ hipError_t backward_mfma(const msr_problem *p, int chunk, const void *Q, const v
 
 // ---- split scores (MSR_FLAG_SPLIT_SCORES) ----------------------------------
 
+// Heads whose decay is below this take the split scores by default.  Under
+// strong decay a row's output comes from a few recent tokens; when their
+// scores are small against |q~||k~|, bf16 rounding of q~ and k~ costs the
+// scores their relative accuracy, and GroupNorm amplifies that on the row.
+// A CPU emulation that rounds only the rotated q~, k~ to bf16 (d_k 64 and
+// 256, T = 256, four seeds) puts the plain path at 7.7e-3 for gamma = 0.9,
+// 1.3e-2 at 0.8, 1.6e-2 at 0.75 and 3.3e-2 at 0.5, against the 2e-2 bf16
+// tolerance; the threshold keeps the plain path where it has margin.
+constexpr float kSplitGamma = 0.9f;
+
+bool strong_decay(const msr_problem *p) {
+    for (int h = 0; h < p->H; ++h)
+        if (p->gamma[h] < kSplitGamma) return true;
+    return false;
+}
+
 bool split_scores(const msr_problem *p, int chunk) {
-    return (p->flags & MSR_FLAG_SPLIT_SCORES) && p->T > MSR_DECODE_MAX_T &&
+    return ((p->flags & MSR_FLAG_SPLIT_SCORES) || strong_decay(p)) && p->T > MSR_DECODE_MAX_T &&
            mfma_supported(p, MSR_FORM_CHUNKWISE, chunk);
+}
+
+// The parallel form under strong decay runs as the chunkwise form with split
+// scores (the forms are equal, state included); the chunk size is the first
+// of 64, 128, 256 the matrix-core path takes for this T, 0 if none.
+int parallel_split_chunk(const msr_problem *p) {
+    if (!strong_decay(p) || p->T <= MSR_DECODE_MAX_T) return 0;
+    for (int b = 64; b <= 256; b *= 2)
+        if (split_scores(p, b)) return b;
+    return 0;
 }
 
 // workspace in front of the chunkwise workspace: Q~ and K~ (scaled) as hi, lo bf16 pairs
@@ -531,9 +557,18 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
     size_t need = generic_plan(p, form, chunk).total;
     size_t mf = mfma_workspace_bytes(p, form, chunk);
     if (form == MSR_FORM_CHUNKWISE && split_scores(p, chunk)) mf += split_plan(p).total;
+    if (form == MSR_FORM_PARALLEL) {
+        const int b = parallel_split_chunk(p);
+        if (b) mf = split_plan(p).total + mfma_workspace_bytes(p, MSR_FORM_CHUNKWISE, b);
+    }
     if (mf > need) need = mf;
     *bytes = need;
     return MSR_OK;
+}
+
+size_t msr_workspace_bytes(const msr_problem *p, int32_t form, int32_t chunk) {
+    size_t n = 0;
+    return msr_workspace_size(p, form, chunk, &n) == MSR_OK ? n : 0;
 }
 
 msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, const void *V,
@@ -552,6 +587,8 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
     if (p->B == 0) return MSR_OK;
     if (p->T == 0) return hip_status(launch_copy_state(c, state_in, state_out, st), "copy state");
 
+    if (const int b = parallel_split_chunk(p))
+        return hip_status(chunkwise_split(p, b, Q, K, V, O, state_in, state_out, ws, st), "split parallel");
     if (mfma_supported(p, MSR_FORM_PARALLEL, p->T))
         return hip_status(mfma_parallel(c, p, Q, K, V, O, state_in, state_out, ws, st), "mfma parallel");
     if (p->T <= MSR_DECODE_MAX_T) {  // a few tokens: the recurrence, one pass over the state

@@ -23,7 +23,7 @@ MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD, MSR_FOR
 STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_ERR_DTYPE",
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
-EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_parallel",
+EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_workspace_bytes", "msr_parallel",
            "msr_chunkwise", "msr_chunkwise_backward", "msr_qkv_projection", "msr_qkv_chunkwise",
            "msr_recurrent_step", "msr_set_kernel_events")
 
@@ -63,6 +63,8 @@ def load():
     lib.msr_last_error.argtypes, lib.msr_last_error.restype = [], ctypes.c_char_p
     lib.msr_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.msr_workspace_size.restype = ctypes.c_int
+    lib.msr_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.c_int32]
+    lib.msr_workspace_bytes.restype = ctypes.c_size_t
     lib.msr_parallel.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msr_parallel.restype = ctypes.c_int
     lib.msr_chunkwise.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msr_abi_version() == 3
+    assert lib.msr_abi_version() == 4
 
 
 def test_problem_struct_layout_matches_the_header():
@@ -64,6 +64,32 @@ def test_invalid_problems_are_rejected(kw, code):
     assert m.STATUS[s] == code
     assert n == 12345  # untouched on error
     assert msr.load().msr_last_error().decode()
+
+
+def test_workspace_bytes_matches_workspace_size():
+    lib = msr.load()
+    for form, chunk in ((m.MSR_FORM_CHUNKWISE, 16), (m.MSR_FORM_PARALLEL, 0), (m.MSR_FORM_STEP, 0),
+                        (m.MSR_FORM_BACKWARD, 16), (m.MSR_FORM_QKV_CHUNKWISE, 16)):
+        d = desc(T=1) if form == m.MSR_FORM_STEP else desc()
+        s, n = status_ws(d, form, chunk)
+        assert s == 0
+        assert lib.msr_workspace_bytes(d.ref, form, chunk) == n
+    # an invalid problem gives 0 and leaves the reason behind
+    assert lib.msr_workspace_bytes(desc(dk=15).ref, m.MSR_FORM_CHUNKWISE, 16) == 0
+    assert b"dk" in lib.msr_last_error()
+
+
+@pytest.mark.parametrize("form,chunk", [(m.MSR_FORM_CHUNKWISE, 64), (m.MSR_FORM_PARALLEL, 0)])
+def test_strong_decay_workspace_covers_the_split_route(form, chunk):
+    # any head with gamma < 0.9 routes a bf16 matrix-core call to split scores,
+    # whose workspace adds Q~ and K~ as hi and lo bf16 parts (4 x B T H dk x 2 bytes)
+    kw = dict(B=1, T=256, H=2, dk=64, dv=64)
+    _, weak = status_ws(desc(**kw, gamma=np.array([0.97, 0.9])), form, chunk)
+    _, strong = status_ws(desc(**kw, gamma=np.array([0.97, 0.5])), form, chunk)
+    assert strong > weak and strong >= 4 * 256 * 2 * 64 * 2
+    _, flag = status_ws(desc(**kw, gamma=np.array([0.97, 0.9]), flags=m.MSR_FLAG_SPLIT_SCORES), m.MSR_FORM_CHUNKWISE, 64)
+    if form == m.MSR_FORM_CHUNKWISE:
+        assert strong == flag
 
 
 def test_chunk_need_not_divide_T():

@@ -41,7 +41,7 @@ def oracle_pairs(q, k, v, gamma, pairs, **kw):
 
 
 # ---------------------------------------------------------------- 7B shape
-PAIRS_7B = [(0, 0), (1, 9), (0, 15)]
+PAIRS_7B = [(0, 0), (1, 9), (0, 15), (1, 3), (1, 15)]
 
 
 @pytest.fixture(scope="module")
@@ -92,6 +92,81 @@ def test_7b_chunk_sizes_agree_on_every_pair(seven_b):
     eo = float((d / r).max())
     es = float(((s1 - s2).abs().amax(dim=(2, 3)) / s2.abs().amax(dim=(2, 3))).max())
     note(f"7B chunk 128 vs 256 over all pairs: O {eo:.2e}  state {es:.2e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+# ------------------------------------------------ 7B shape, parallel form
+PAIRS_PAR = [(0, 0), (0, 7), (1, 3), (1, 15)]
+ROWS_PAR = [0, 1, 127, 128, 129, 4095, 4096, 8191]
+
+
+def run_parallel_like_bench(w, q, k, v, g, s_in=None):
+    """The benchmark's msr_parallel call: preallocated output, state, workspace."""
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    qd, kd, vd = (up(x, w.dtype, dev) for x in (q, k, v))
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=qd.dtype, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    sd = None if s_in is None else torch.from_numpy(s_in).to(dev)
+    ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g,
+                                        msr.MSR_FORM_PARALLEL, 0), dtype=torch.uint8, device=dev)
+    msr.msr_parallel(qd, kd, vd, g, out=o, state_in=sd, state_out=s, workspace=ws)
+    torch.cuda.synchronize()
+    return o, s
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_7b_parallel_sampled_rows_vs_oracle(seven_b, with_state):
+    # rows at chunk-like boundaries and at the far end, where gamma^(n-m)
+    # underflows fp32 for all but the slowest heads
+    w, q, k, v, g, ref = seven_b
+    s_in = mi.state(w, 0.05) if with_state else None
+    note(f"7B parallel (state in: {with_state}): gpu")
+    o, s = run_parallel_like_bench(w, q, k, v, g, s_in)
+    for (b, h) in PAIRS_PAR:
+        ro = orc.parallel_rows(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], g[h], ROWS_PAR,
+                               s_in=None if s_in is None else s_in[b, h])
+        eo = slice_err(down(o[b, ROWS_PAR, h, :]), ro)
+        note(f"  pair ({b},{h}) rows {ROWS_PAR}: O err {eo:.2e}")
+        assert eo < TOL["bf16"]
+    # the outgoing state on the pairs the module's oracle ran (zero incoming state)
+    if not with_state:
+        for (b, h), (_, rs) in ref.items():
+            es = slice_err(down(s[b, h]), rs)
+            note(f"  pair ({b},{h}): state err {es:.2e}")
+            assert es < TOL["bf16"]
+
+
+def test_7b_parallel_state_in_full_pairs_vs_oracle(seven_b):
+    # two whole pairs with an incoming state: gamma^T S_in matters on head 15
+    # (gamma^8192 ~ 0.992) and underflows on head 0
+    w, q, k, v, g, _ = seven_b
+    s_in = mi.state(w, 0.05)
+    pairs = [(0, 0), (1, 15)]
+    note("7B parallel with state: oracle on", pairs)
+    ref = oracle_pairs(q, k, v, g, pairs, s_in=s_in)
+    o, s = run_parallel_like_bench(w, q, k, v, g, s_in)
+    for (b, h), (ro, rs) in ref.items():
+        eo = slice_err(down(o[b, :, h, :]), ro)
+        es = slice_err(down(s[b, h]), rs)
+        note(f"  pair ({b},{h}): O err {eo:.2e}  state err {es:.2e}")
+        assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+def test_7b_parallel_agrees_with_chunkwise_on_every_pair(seven_b):
+    w, q, k, v, g, _ = seven_b
+    s_in = mi.state(w, 0.05)
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    o1, s1 = run_parallel_like_bench(w, q, k, v, g, s_in)
+    qd, kd, vd = (up(x, w.dtype, dev) for x in (q, k, v))
+    o2, s2 = msr.msr_chunkwise(qd, kd, vd, g, 128, state_in=torch.from_numpy(s_in).to(dev))
+    torch.cuda.synchronize()
+    d = (o1.float() - o2.float()).abs().amax(dim=(1, 3))
+    r = o2.float().abs().amax(dim=(1, 3))
+    eo = float((d / r).max())
+    es = float(((s1 - s2).abs().amax(dim=(2, 3)) / s2.abs().amax(dim=(2, 3))).max())
+    note(f"7B parallel vs chunkwise 128 over all pairs: O {eo:.2e}  state {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
