@@ -93,7 +93,46 @@ def chunk_kernel_flops(T, H, B, dk, dv, b):
 
 
 def chunk_bytes(T, H, B, dk, dv):
-    return B * T * H * (2 * dk + 2 * dv) * 2
+    """Algorithmic HBM bytes of a bf16 forward: Q, K, V read and O written
+    once, plus the fp32 outgoing state."""
+    return B * T * H * (2 * dk + 2 * dv) * 2 + B * H * dk * dv * 4
+
+
+FLUSH_MIB = 512  # larger than the 256 MiB last-level (MALL) cache
+
+
+class Flusher:
+    """Writes a 512 MiB scratch buffer, so that no input of the next call is
+    still held in the L2 or last-level cache."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(FLUSH_MIB << 18, dtype=torch.float32, device="cuda:0")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(float(self.i))
+
+
+def per_call_ms(torch, fn, reps, flush=None):
+    """Event-timed duration of each of `reps` calls of fn (a flush, untimed,
+    before each when given).  Returns the list of milliseconds."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def stats_ms(ms):
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"median_ms": float(np.median(ms)), "min_ms": float(ms.min()), "mean_ms": float(ms.mean()),
+            "reps": int(ms.size)}
 
 
 # The sources each measured kernel is built from: its own file, the shared
@@ -130,6 +169,28 @@ def traffic_record(kernel):
     return rec.get("bytes_per_launch")
 
 
+def call_traffic_record(chunk):
+    """HBM bytes of one whole 7B-shaped msr_chunkwise call (every kernel),
+    from the committed counter runs, if taken on the current sources."""
+    p = ROOT / "profiles" / "traffic.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text()).get("chunkwise_call_b%d" % chunk)
+    if not rec or rec.get("source_sha") != library_source_sha():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def library_source_sha():
+    """Hash of every library source and the build script."""
+    csrc = ROOT / "retnet_scale_retention_amd" / "csrc"
+    h = hashlib.sha256()
+    for f in sorted(csrc.glob("*.hip")) + sorted(csrc.glob("*.hpp")) + sorted(csrc.glob("*.cpp")):
+        h.update(f.read_bytes())
+    h.update((ROOT / "retnet_scale_retention_amd" / "build.py").read_bytes())
+    return h.hexdigest()[:16]
+
+
 def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     w = mi.WORKLOADS["7b"]
     dev = torch.device("cuda:0")
@@ -145,20 +206,27 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     for _ in range(warmup):
         msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
     ev = HipEvents(steps)
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
         msr.set_kernel_events(*ev.pairs[i])
+        calls[i][0].record()
         msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+        calls[i][1].record()
     msr.set_kernel_events(None, None)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     kern_ms = [ev.elapsed_ms(i) for i in range(steps)]
+    call_ms = [a.elapsed_time(b) for a, b in calls]
     ev.close()
     ms = total_ms / steps
+    # the same call with a 512 MiB cache flush before each rep
+    flushed = stats_ms(per_call_ms(torch, lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s,
+                                                                    workspace=ws), steps, Flusher(torch)))
     # the same call with the split-scores precision option
     wss = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, chunk,
                                          flags=msr.MSR_FLAG_SPLIT_SCORES), dtype=torch.uint8, device=dev)
@@ -194,6 +262,7 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
                         "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, ochunk) / (other_ms / 1e3) / 1e12},
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
         "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
+        "call": stats_ms(call_ms), "kernel": stats_ms(kern_ms), "flushed": flushed,
     }
 
 
@@ -212,21 +281,51 @@ def bench_long(torch, msr, mi, calls):
     out = {"config": {"B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv}}
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    nbytes = chunk_bytes(w.T, w.H, w.B, w.dk, w.dv)
+    out["bytes_per_call"] = nbytes
     for chunk in w.chunks:
         ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE,
                                             chunk), dtype=torch.uint8, device=dev)
-        msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(calls):
-            msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / calls
+        fn = lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+        fn()
+        st = stats_ms(per_call_ms(torch, fn, calls))
+        ms = st["median_ms"]
         del ws
-        out["b%d" % chunk] = {"ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
-                              "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk) / (ms / 1e3) / 1e12}
+        out["b%d" % chunk] = {"ms_per_call": ms, **st, "tokens_per_s": w.B * w.T / (ms / 1e3),
+                              "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk) / (ms / 1e3) / 1e12,
+                              "hbm_GBs": nbytes / (ms / 1e3) / 1e9,
+                              "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
     return out
+
+
+def bench_small(torch, msr, mi, reps):
+    """The small model layer (B=4, T=2048, H=8, d_k=d_v=64, chunk 64, bf16):
+    its 34 MB of inputs and outputs fit the last-level cache, so a 512 MiB
+    flush precedes every timed call."""
+    w = mi.WORKLOADS["small"]
+    dev = torch.device("cuda:0")
+    q, k, v = mi.qkv(w)
+    up = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    qd, kd, vd = up(q), up(k), up(v)
+    g = mi.gammas(w.H)
+    chunk = w.chunks[0]
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE,
+                                               chunk)), dtype=torch.uint8, device=dev)
+    fn = lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+    for _ in range(3):
+        fn()
+    fl = stats_ms(per_call_ms(torch, fn, reps, Flusher(torch)))
+    warm = stats_ms(per_call_ms(torch, fn, reps))
+    nbytes = chunk_bytes(w.T, w.H, w.B, w.dk, w.dv)
+    ms = fl["median_ms"]
+    return {"config": {"workload": "small model layer", "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                       "chunk": chunk, "dtype": "bf16"},
+            "flushed": fl, "warm": warm, "tokens_per_s": w.B * w.T / (ms / 1e3),
+            "bytes_per_call": nbytes, "hbm_GBs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk) / (ms / 1e3) / 1e12}
 
 
 def bench_parallel(torch, msr, mi, steps):
@@ -379,6 +478,25 @@ def bench_decode(torch, msr, mi, nsteps):
     kms = float(np.mean(kern))
     bytes_step = 2 * w.B * w.H * w.dk * w.dv * 4 + w.B * w.H * (2 * w.dk + 2 * w.dv) * 2
 
+    # the same step loop captured once in a HIP graph (each step's position is
+    # a kernel argument of its own node), replayed: no host launch gaps
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for i in range(nsteps):
+            msr.msr_recurrent_step(qs[i], ks[i], vs[i], state, g, w.T + i, out=o)
+    gph.replay()
+    torch.cuda.synchronize()
+    graph_ms = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms.append(a.elapsed_time(b) / nsteps)
+    del gph
+    gstep = float(np.median(graph_ms))
+
     # batched serving: every sequence at its own position (one per batch row)
     nr = max(8, nsteps // 8)
     base = torch.tensor([(b * 37) % 4096 for b in range(w.B)], dtype=torch.int64, device=dev)
@@ -410,8 +528,12 @@ def bench_decode(torch, msr, mi, nsteps):
     mms = (time.perf_counter() - tm0) * 1e3 / nm
     return {
         "config": {"B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "prefill_tokens": w.T, "steps": nsteps},
-        "steps_per_s": 1e3 / step_ms, "tokens_per_s": w.B * 1e3 / step_ms,
-        "ms_per_step": step_ms, "kernel_us": kms * 1e3,
+        "note": "steps_per_s: wall time of the step loop captured in a HIP graph and replayed (median of 3 "
+                "replays); eager: the same loop launched from the host",
+        "steps_per_s": 1e3 / gstep, "tokens_per_s": w.B * 1e3 / gstep, "ms_per_step": gstep,
+        "wall_hbm_frac": bytes_step / (gstep / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "eager": {"steps_per_s": 1e3 / step_ms, "ms_per_step": step_ms},
+        "kernel_us": kms * 1e3,
         "hbm": {"achieved": bytes_step / (kms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": bytes_step / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": bytes_step,
                 "traffic": traffic_record("decode_kernel")},
@@ -458,6 +580,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -478,7 +601,8 @@ def main():
 
     r = bench_chunkwise(torch, msr, mi, args.steps, args.warmup, args.chunk)
     w = r["workload"]
-    lng = None if args.no_long else bench_long(torch, msr, mi, 3)
+    lng = None if args.no_long else bench_long(torch, msr, mi, 7)
+    sml = None if args.no_small else bench_small(torch, msr, mi, 20)
     dec = None if args.no_decode else bench_decode(torch, msr, mi, args.decode_steps)
     par = None if args.no_parallel else bench_parallel(torch, msr, mi, 3)
     bwd = None
@@ -518,6 +642,16 @@ def main():
                      "traffic": traffic, "kernel": main_kernel,
                      "kernel_us": r["kernel_ms"] * 1e3, "flops_per_launch": r["kernel_flops"]},
         "step_tflops": r["step_tflops"], "step_mfma_frac": r["step_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+        "call_roofline": {
+            "note": "the whole call (every kernel of one msr_chunkwise), algorithmic flops "
+                    "(b+1)(dk+dv) + 4 dk dv per token-head over the event-timed call; traffic: the call's "
+                    "counter bytes (all kernels) against its algorithmic bytes",
+            "achieved": r["flops"] / (r["call"]["median_ms"] / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": r["flops"] / (r["call"]["median_ms"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "flops_per_call": r["flops"], "algorithmic_bytes": r["bytes"],
+            "traffic": call_traffic_record(r["chunk"])},
+        "timing": {"call": r["call"], "kernel": r["kernel"], "flushed_call": r["flushed"]},
+        "small_layer": sml,
         "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",
                          "ms_per_step": r["split_scores_ms"]},
         "other_chunk": r["other_chunk"],

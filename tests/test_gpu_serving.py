@@ -176,3 +176,38 @@ def test_short_calls_vs_oracle(T, dtype, form, with_state):
     assert eo < TOL[dtype] and es < TOL[dtype]
     if sd is not None:  # the incoming state is left untouched
         assert np.array_equal(down(sd), s_in.astype(np.float64))
+
+
+def test_decode_steps_captured_in_a_hip_graph_match_eager():
+    # the benchmark's decode loop runs as one captured HIP graph; every replay
+    # (with eager work and synchronisations between replays) must reproduce
+    # the eagerly launched steps bit for bit
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    B, H, dk, dv, n = 4, 2, 128, 256, 6
+    w = mi.Workload("graph-decode", 95, B, 1, H, dk, dv, "bf16", (1,))
+    g = mi.gammas(H)
+    s0 = torch.from_numpy(mi.state(w, 0.1)).to(dev)
+    qs = mi.device_normal((n, B, H, dk), 9501, dev, torch.bfloat16)
+    ks = mi.device_normal((n, B, H, dk), 9502, dev, torch.bfloat16)
+    vs = mi.device_normal((n, B, H, dv), 9503, dev, torch.bfloat16)
+    st_e = s0.clone()
+    outs_e = [msr.msr_recurrent_step(qs[i], ks[i], vs[i], st_e, g, 10 + i) for i in range(n)]
+    st_g = s0.clone()
+    outs_g = [torch.empty_like(outs_e[0]) for _ in range(n)]
+    torch.cuda.synchronize()
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for i in range(n):
+            msr.msr_recurrent_step(qs[i], ks[i], vs[i], st_g, g, 10 + i, out=outs_g[i])
+    for rep in range(3):
+        st_g.copy_(s0)
+        for t in outs_g:
+            t.zero_()
+        torch.cuda.synchronize()
+        gph.replay()
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        for i in range(n):
+            assert torch.equal(outs_g[i], outs_e[i]), (rep, i)
+        assert torch.equal(st_g, st_e), rep
