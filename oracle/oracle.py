@@ -28,19 +28,30 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "oracle.c"
-_LIB = _HERE / "liboracle.so"
+# MSR_ORACLE_LIB selects another build of oracle.c (the sanitized one of
+# tests/test_sanitized_cpu.py); the default is the gcc build below
+_LIB = Path(os.environ.get("MSR_ORACLE_LIB", _HERE / "liboracle.so"))
+_ASAN_LIB = _HERE / "liboracle_asan.so"
 _lib = None
 
 
-def build(force: bool = True) -> Path:
-    """Compile oracle.c with gcc (IEEE arithmetic: no fast-math)."""
-    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
-        tmp = _LIB.with_suffix(".so.tmp")
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               str(_SRC), "-o", str(tmp), "-lm"]
+def build(force: bool = True, sanitize: bool = False) -> Path:
+    """Compile oracle.c with gcc (IEEE arithmetic: no fast-math).  With
+    sanitize: with clang and AddressSanitizer + UndefinedBehaviorSanitizer
+    into liboracle_asan.so (the runtime clang's hipcc builds use too)."""
+    lib = _ASAN_LIB if sanitize else _LIB
+    if force or not lib.exists() or lib.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = lib.with_suffix(".so.tmp")
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                   "-fno-omit-frame-pointer", str(_SRC), "-o", str(tmp), "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                   str(_SRC), "-o", str(tmp), "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 class _Problem(ctypes.Structure):
