@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-/* 4: msr_workspace_bytes; strong-decay routing (3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection,
+/* 4: msr_workspace_bytes, msr_chunkwise_noalloc; strong-decay routing (3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection,
  * msr_qkv_chunkwise; 2: pos_rows) */
 #define MSR_ABI_VERSION 4
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
@@ -187,6 +187,24 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
 msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
                          const void *V, void *O, const float *state_in, float *state_out,
                          void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * msr_chunkwise without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and rules as
+ * msr_chunkwise; the scratch memory comes from a fixed array of
+ * MSR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The call itself allocates nothing.
+ *   - A problem whose msr_workspace_size(p, MSR_FORM_CHUNKWISE, chunk) exceeds
+ *     that size is rejected with MSR_ERR_WORKSPACE before anything runs.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (different streams, or different host threads) race and give
+ *     wrong results.  Order them on one stream.
+ */
+#define MSR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+msr_status msr_chunkwise_noalloc(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
+                                 const void *V, void *O, const float *state_in, float *state_out,
+                                 void *hip_stream);
 
 /*
  * Backward pass of the chunkwise form (equivalently of the parallel form):

@@ -646,6 +646,28 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
     return hip_status(generic_chunkwise(p, chunk, Q, K, V, O, state_in, state_out, ws, st), "generic chunkwise");
 }
 
+msr_status msr_chunkwise_noalloc(const msr_problem *p, int32_t chunk, const void *Q, const void *K,
+                                 const void *V, void *O, const float *state_in, float *state_out,
+                                 void *hip_stream) {
+    msr_status s = check_problem(p, false);
+    if (s != MSR_OK) return s;
+    if ((s = check_tensors(p, Q, K, V, O, state_in, state_out)) != MSR_OK) return s;
+    size_t need = 0;
+    if ((s = msr_workspace_size(p, MSR_FORM_CHUNKWISE, chunk, &need)) != MSR_OK) return s;
+    if (need > MSR_STATIC_SCRATCH_BYTES)
+        return fail(MSR_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch, more than the %zu of the fixed array "
+                    "msr_chunkwise_noalloc uses (call msr_chunkwise with a workspace instead)",
+                    need, MSR_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0 && (size_t)p->B * p->T > 0) {
+        const hipError_t e = static_scratch(&ws);
+        if (e != hipSuccess) return hip_status(e, "scratch address");
+    }
+    return msr_chunkwise(p, chunk, Q, K, V, O, state_in, state_out, ws, ws ? MSR_STATIC_SCRATCH_BYTES : 0,
+                         hip_stream);
+}
+
 msr_status msr_qkv_projection(const msr_problem *p, int32_t d_model, const void *X, const void *Wq,
                               const void *Wk, const void *Wv, void *Q, void *K, void *V, void *hip_stream) {
     msr_status s = check_qkv(p, d_model, X, Wq, Wk, Wv);

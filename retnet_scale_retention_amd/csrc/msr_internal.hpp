@@ -88,6 +88,11 @@ hipError_t launch_accumulate(size_t n, const void *x, int in_dtype, float *y, in
 hipError_t launch_state_op(const MsrConst &c, int d1, int d2, const float *in, float *out, int transpose,
                            float power, int j0, int nj, hipStream_t st);
 
+// The fixed scratch array of msr_chunkwise_noalloc (k_static.hip): this
+// device's copy, looked up once per device.
+constexpr size_t MSR_STATIC_SCRATCH_BYTES = MSR_NOALLOC_SCRATCH_BYTES;
+hipError_t static_scratch(void **ptr);
+
 // Measurement hook (msr_set_kernel_events): records the caller's events
 // around the main kernel of a call on its stream.  No-ops when unset.
 void main_kernel_begin(hipStream_t st);

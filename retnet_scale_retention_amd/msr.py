@@ -24,7 +24,7 @@ STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
 EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_workspace_bytes", "msr_parallel",
-           "msr_chunkwise", "msr_chunkwise_backward", "msr_qkv_projection", "msr_qkv_chunkwise",
+           "msr_chunkwise", "msr_chunkwise_noalloc", "msr_chunkwise_backward", "msr_qkv_projection", "msr_qkv_chunkwise",
            "msr_recurrent_step", "msr_set_kernel_events")
 
 
@@ -69,6 +69,8 @@ def load():
     lib.msr_parallel.restype = ctypes.c_int
     lib.msr_chunkwise.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.msr_chunkwise.restype = ctypes.c_int
+    lib.msr_chunkwise_noalloc.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
+    lib.msr_chunkwise_noalloc.restype = ctypes.c_int
     lib.msr_chunkwise_backward.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.c_size_t, vp]
     lib.msr_chunkwise_backward.restype = ctypes.c_int
@@ -210,6 +212,28 @@ def msr_chunkwise(q, k, v, gamma, chunk, *, theta=None, scale=0.0, eps=1e-5, pos
     than `chunk` takes the remaining tokens when chunk does not divide T)."""
     return _form(load().msr_chunkwise, MSR_FORM_CHUNKWISE, q, k, v, gamma, chunk, theta, scale,
                  eps, pos0, flags, state_in, return_state, out, state_out, workspace, stream, pos_rows)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MSR_NOALLOC_SCRATCH_BYTES
+
+
+def msr_chunkwise_noalloc(q, k, v, gamma, chunk, *, out, state_out=None, theta=None, scale=0.0, eps=1e-5, pos0=0,
+                          flags=0, state_in=None, stream=None, pos_rows=None):
+    """msr_chunkwise with the library's fixed per-GPU scratch array instead of
+    a workspace: allocates nothing (out and state_out are the caller's).
+    Returns (O, state_out)."""
+    torch = _torch()
+    B, T, H, dk, dv = _prep(q, k, v)
+    d = _Desc(B, T, H, dk, dv, _dtype_code(q), gamma, theta, scale, eps, pos0, flags,
+              _pos_rows(pos_rows, B, q.device))
+    if tuple(out.shape) != (B, T, H, dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, T, H, dv] tensor of q's dtype")
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, dk, dv)):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, dk, dv] tensor")
+    _check(load().msr_chunkwise_noalloc(d.ref, int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_in),
+                                        _ptr(state_out), _stream(q, stream)))
+    return out, state_out
 
 
 def msr_chunkwise_backward(q, k, v, gamma, chunk, grad_out, *, grad_state=None, state_in=None, theta=None,
