@@ -65,9 +65,9 @@
 extern "C" {
 #endif
 
-/* 4: msr_workspace_bytes, msr_chunkwise_noalloc; strong-decay routing (3: MSR_FLAG_DECAY_ROWNORM, msr_qkv_projection,
- * msr_qkv_chunkwise; 2: pos_rows) */
-#define MSR_ABI_VERSION 4
+/* 5: MSR_FLAG_FUSED (4: msr_workspace_bytes, msr_chunkwise_noalloc; strong-decay routing; 3: MSR_FLAG_DECAY_ROWNORM,
+ * msr_qkv_projection, msr_qkv_chunkwise; 2: pos_rows) */
+#define MSR_ABI_VERSION 5
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
 #define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
 #define MSR_MAX_DV 1024   /* d_v limit */
@@ -108,11 +108,23 @@ typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
  * then runs as the equal chunkwise form with chunk 64, 128 or 256).  Costs a
  * rotation pass and three score products instead of one.
  */
+/*
+ * FUSED (a schedule option of the bf16 matrix-core path of msr_chunkwise,
+ * same results to within the bf16 tolerance): the rotation, the intra-chunk
+ * scores and, when d_v is 256, GroupNorm run inside the recurrence
+ * workgroups, from Q and K staged in LDS, instead of in separate passes
+ * through HBM.  It moves about half the bytes of the default schedule but
+ * is slower on MI355X at the shapes measured (its per-chunk vector work and
+ * workgroup barriers outweigh the traffic saved), so it is not the default.
+ * Taken for bf16, d_k 128 or 256, chunk 64 or 128, d_v a multiple of 256,
+ * without SPLIT_SCORES, DECAY_ROWNORM or a gamma below 0.9; ignored otherwise.
+ */
 enum {
     MSR_FLAG_NO_ROTATE = 1u,
     MSR_FLAG_NO_GROUPNORM = 2u,
     MSR_FLAG_DECAY_ROWNORM = 4u,
-    MSR_FLAG_SPLIT_SCORES = 8u
+    MSR_FLAG_SPLIT_SCORES = 8u,
+    MSR_FLAG_FUSED = 16u
 };
 
 /* forms, for msr_workspace_size */

@@ -1544,8 +1544,9 @@ hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, bool wide, int chu
 struct MfmaPlan {
     size_t qf = 0, kf = 0, pf = 0, stats = 0, segE = 0, total = 0;
     int nseg = 1;
-    int NS = 1;         // GroupNorm partials per row
-    bool wide = false;  // 256-column slices (k_chunk_wide.hip)
+    int NS = 1;          // GroupNorm partials per row
+    bool wide = false;   // 256-column slices (k_chunk_wide.hip)
+    bool fused = false;  // the fused kernel (k_chunk_fused.hip): no fragments
 };
 
 // Segments per pair: doubled while the workgroups (pairs x value slices x
@@ -1558,11 +1559,23 @@ int choose_nseg(const msr_problem *p, int chunk, int slice_cols) {
     return g;
 }
 
-// workspace: [QF][KF][PF][slice statistics]
-MfmaPlan mfma_plan(const msr_problem *p, int chunk) {
+// workspace: [QF][KF][PF][slice statistics][segment states]; the fused
+// kernel (split = false: the caller's Q and K, no low parts) needs only
+// [slice statistics][segment states]
+MfmaPlan mfma_plan(const msr_problem *p, int chunk, bool split = false) {
     MfmaPlan m;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t tokens = (size_t)p->B * p->T * p->H;  // token-heads
+    if (!split && (p->flags & MSR_FLAG_FUSED) && chunk_fused_supported(p->dk, p->dv, chunk) &&
+        !(p->flags & (kFlagNoWide | MSR_FLAG_DECAY_ROWNORM))) {
+        m.fused = true;
+        m.NS = p->dv / 256;
+        m.stats = 0;  // partials of 32 columns when the rows span several slices
+        m.segE = m.NS > 1 ? up(tokens * (p->dv / 32) * sizeof(float2)) : 0;
+        m.nseg = choose_nseg(p, chunk, 256);
+        m.total = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
+        return m;
+    }
     m.qf = 0;
     m.kf = m.qf + up(tokens * p->dk * 2);
     m.pf = m.kf + up(tokens * p->dk * 2);
@@ -1674,16 +1687,46 @@ bool mfma_supported(const msr_problem *p, int form, int chunk) {
     return true;
 }
 
-size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk) {
+size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk, bool split) {
     if (!mfma_supported(p, form, chunk)) return 0;
-    return form == MSR_FORM_PARALLEL ? par_plan(p).total : mfma_plan(p, chunk).total;
+    return form == MSR_FORM_PARALLEL ? par_plan(p).total : mfma_plan(p, chunk, split).total;
 }
 
 hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, const void *Q,
                           const void *K, const void *V, void *O, const float *s_in, float *s_out,
                           void *ws, hipStream_t st, const void *Qlo, const void *Klo) {
-    const MfmaPlan m = mfma_plan(p, chunk);
+    const MfmaPlan m = mfma_plan(p, chunk, Qlo != nullptr);
     char *wsb = static_cast<char *>(ws);
+    if (m.fused) {
+        FusedArgs f{};
+        f.q = static_cast<const uint16_t *>(Q);
+        f.k = static_cast<const uint16_t *>(K);
+        f.v = static_cast<const uint16_t *>(V);
+        f.o = static_cast<uint16_t *>(O);
+        f.s_in = s_in;
+        f.s_out = s_out;
+        f.stats = m.NS > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
+        f.NS = m.NS;
+        f.NW2 = m.NS;
+        f.NP = p->dv / 32;
+        f.nseg = m.nseg;
+        f.seglen = p->T / chunk / m.nseg;
+        f.segE = m.nseg > 1 ? reinterpret_cast<float *>(wsb + m.segE) : nullptr;
+        hipError_t e = hipSuccess;
+        if (m.nseg > 1 && (e = launch_chunk_fused(c, f, chunk, true, st)) != hipSuccess) return e;
+        main_kernel_begin(st);
+        e = launch_chunk_fused(c, f, chunk, false, st);
+        main_kernel_end(st);
+        if (e != hipSuccess) return e;
+        if (m.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+            const size_t rows = (size_t)p->B * p->T * p->H;
+            const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
+            hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, f.NP, f.stats, f.o,
+                               rows);
+            e = hipGetLastError();
+        }
+        return e;
+    }
     ChunkArgs a{};  // every field starts at zero (par = 0: chunkwise form)
     a.qf = reinterpret_cast<const uint16_t *>(wsb + m.qf);
     a.kf = reinterpret_cast<const uint16_t *>(wsb + m.kf);

@@ -64,7 +64,7 @@ msr_status check_problem(const msr_problem *p, bool T1) {
     if (p->pos_rows && (reinterpret_cast<uintptr_t>(p->pos_rows) & 7u))
         return fail(MSR_ERR_INVALID_ARG, "pos_rows is not 8-byte aligned");
     if (p->flags & ~(uint32_t)(MSR_FLAG_NO_ROTATE | MSR_FLAG_NO_GROUPNORM | MSR_FLAG_DECAY_ROWNORM |
-                               MSR_FLAG_SPLIT_SCORES))
+                               MSR_FLAG_SPLIT_SCORES | MSR_FLAG_FUSED))
         return fail(MSR_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     return MSR_OK;
 }
@@ -556,10 +556,11 @@ msr_status msr_workspace_size(const msr_problem *p, int32_t form, int32_t chunk,
     }
     size_t need = generic_plan(p, form, chunk).total;
     size_t mf = mfma_workspace_bytes(p, form, chunk);
-    if (form == MSR_FORM_CHUNKWISE && split_scores(p, chunk)) mf += split_plan(p).total;
+    if (form == MSR_FORM_CHUNKWISE && split_scores(p, chunk))
+        mf = split_plan(p).total + mfma_workspace_bytes(p, form, chunk, true);
     if (form == MSR_FORM_PARALLEL) {
         const int b = parallel_split_chunk(p);
-        if (b) mf = split_plan(p).total + mfma_workspace_bytes(p, MSR_FORM_CHUNKWISE, b);
+        if (b) mf = split_plan(p).total + mfma_workspace_bytes(p, MSR_FORM_CHUNKWISE, b, true);
     }
     if (mf > need) need = mf;
     *bytes = need;

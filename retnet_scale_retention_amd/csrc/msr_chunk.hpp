@@ -33,6 +33,29 @@ struct ChunkArgs {
     int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
 };
 
+// Argument block of the fused chunk kernel (k_chunk_fused.hip), which reads
+// the caller's Q, K and V directly.
+struct FusedArgs {
+    const uint16_t *q, *k, *v;  // [B][T][H][d_k], [B][T][H][d_k], [B][T][H][d_v] bf16
+    uint16_t *o;                // [B][T][H][d_v] bf16
+    const float *s_in;
+    float *s_out;
+    float2 *stats;  // [B*T*H][NP] (mean, M2) of each wave's 32 columns (NS > 1)
+    int NS;         // 256-column slices per pair (d_v / 256)
+    int NW2;        // workgroup slices per pair (= NS)
+    int NP;         // GroupNorm partials per row (d_v / 32)
+    int nseg, seglen;  // segments of seglen chunks per pair
+    float *segE;       // [pair][nseg][dk][dv] segment end states from a zero state
+};
+
+// The fused chunk kernel takes d_k 128 or 256, b 64 or 128, d_v a multiple
+// of 256.
+bool chunk_fused_supported(int dk, int dv, int bc);
+
+// Launches it over pairs x a.NW2 x a.nseg workgroups: the state-only pass
+// (segment end states) or the full pass.
+hipError_t launch_chunk_fused(const MsrConst &c, const FusedArgs &a, int bc, bool state_only, hipStream_t st);
+
 // Problem flag set only on the library's own sub-problems (the public entry
 // points reject it like any unknown flag): keep the chunk recurrence on the
 // 64-column kernels.  The backward pass sets it on its retention calls, for

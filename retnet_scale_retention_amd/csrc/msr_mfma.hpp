@@ -6,8 +6,9 @@
 // True when the MFMA kernels handle this problem/form/chunk.
 bool mfma_supported(const msr_problem *p, int form, int chunk);
 
-// Workspace the MFMA path needs (0 when it is not used for this problem).
-size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk);
+// Workspace the MFMA path needs (0 when it is not used for this problem);
+// split: the chunkwise form with split scores (low parts of Q~, K~ given)
+size_t mfma_workspace_bytes(const msr_problem *p, int form, int chunk, bool split = false);
 
 // Qlo, Klo (optional, both or neither): low parts of two-term bf16 splits of
 // Q and K; the intra-chunk scores then take hi.hi + lo.hi + hi.lo

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msr_abi_version() == 4
+    assert lib.msr_abi_version() == 5
 
 
 def test_problem_struct_layout_matches_the_header():
@@ -57,7 +57,7 @@ def status_ws(d, form=m.MSR_FORM_CHUNKWISE, chunk=16):
     (dict(gamma=np.array([0.9, 0.0, 0.9, 0.9])), "MSR_ERR_INVALID_ARG"),
     (dict(gamma=np.array([0.9, np.nan, 0.9, 0.9])), "MSR_ERR_INVALID_ARG"),
     (dict(eps=-1.0), "MSR_ERR_INVALID_ARG"), (dict(pos0=-3), "MSR_ERR_INVALID_ARG"),
-    (dict(flags=16), "MSR_ERR_INVALID_ARG"), (dict(scale=float("inf")), "MSR_ERR_INVALID_ARG"),
+    (dict(flags=32), "MSR_ERR_INVALID_ARG"), (dict(scale=float("inf")), "MSR_ERR_INVALID_ARG"),
 ])
 def test_invalid_problems_are_rejected(kw, code):
     s, n = status_ws(desc(**kw))

@@ -55,7 +55,7 @@ def seven_b():
     return w, q, k, v, g, ref
 
 
-def run_chunkwise_like_bench(w, q, k, v, g, chunk):
+def run_chunkwise_like_bench(w, q, k, v, g, chunk, flags=0):
     """Same call as the benchmark: preallocated output, state and workspace."""
     torch, dev = torch_dev()
     import retnet_scale_retention_amd as msr
@@ -63,17 +63,20 @@ def run_chunkwise_like_bench(w, q, k, v, g, chunk):
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=qd.dtype, device=dev)
     s = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g,
-                                        msr.MSR_FORM_CHUNKWISE, chunk), dtype=torch.uint8, device=dev)
-    msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
+                                        msr.MSR_FORM_CHUNKWISE, chunk, flags=flags), dtype=torch.uint8, device=dev)
+    msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws, flags=flags)
     torch.cuda.synchronize()
     return o, s
 
 
-@pytest.mark.parametrize("chunk", [128, 256])
-def test_7b_sampled_pairs_vs_oracle(seven_b, chunk):
+FUSED = 16  # MSR_FLAG_FUSED: the fused schedule of the chunkwise form
+
+
+@pytest.mark.parametrize("chunk,flags", [(128, 0), (256, 0), (128, FUSED)])
+def test_7b_sampled_pairs_vs_oracle(seven_b, chunk, flags):
     w, q, k, v, g, ref = seven_b
-    note(f"7B chunk {chunk}: gpu")
-    o, s = run_chunkwise_like_bench(w, q, k, v, g, chunk)
+    note(f"7B chunk {chunk} flags {flags}: gpu")
+    o, s = run_chunkwise_like_bench(w, q, k, v, g, chunk, flags)
     for (b, h), (ro, rs) in ref.items():
         eo = slice_err(down(o[b, :, h, :]), ro)
         es = slice_err(down(s[b, h]), rs)
@@ -226,11 +229,11 @@ def long_seq():
     return w, q, k, v, g, ref
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 256])
-def test_long_sampled_pairs_vs_oracle(long_seq, chunk):
+@pytest.mark.parametrize("chunk,flags", [(64, 0), (128, 0), (256, 0), (64, FUSED), (128, FUSED)])
+def test_long_sampled_pairs_vs_oracle(long_seq, chunk, flags):
     w, q, k, v, g, ref = long_seq
-    note(f"long chunk {chunk}: gpu")
-    o, s = run_chunkwise_like_bench(w, q, k, v, g, chunk)
+    note(f"long chunk {chunk} flags {flags}: gpu")
+    o, s = run_chunkwise_like_bench(w, q, k, v, g, chunk, flags)
     for (b, h), (ro, rs) in ref.items():
         eo = slice_err(down(o[b, :, h, :]), ro)
         es = slice_err(down(s[b, h]), rs)
