@@ -22,13 +22,16 @@ already resident in HBM.  The same JSON line also reports
   - qkv: the Q/K/V projections (d_model = 4096) with the rotation in the
     GEMM epilogue, and the projections + chunkwise form together;
   - other_chunk: the same forward at the workload's other chunk size (256);
+  - fused_schedule: the same forward with MSR_FLAG_FUSED (rotation, scores and
+    GroupNorm inside the recurrence workgroups; fewer HBM bytes, not the
+    default), here and at the long sequence's chunks 64 and 128;
   - long_sequence: the chunkwise forward over B=1, T=131072, H=8, d_k=128,
     d_v=256 at chunk 64, 128 and 256 (state carried across all chunks);
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
     of the same workload on the host cores (a reported baseline only).
 Inputs are synthetic and seeded.  Usage:
   python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward]
-                  [--no-qkv] [--no-long] [--copy-mib N]
+                  [--no-qkv] [--no-long] [--no-small] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -141,6 +144,7 @@ KERNEL_SOURCES = {
     "chunk_mfma_kernel": "k_chunk_mfma.hip",
     "chunk_ws_kernel": "k_chunk_mfma.hip",
     "chunk_wide_kernel": "k_chunk_wide.hip",
+    "chunk_fused_kernel": "k_chunk_fused.hip",
     "prep_kernel": "k_chunk_mfma.hip",
     "gn_finalize_kernel": "k_chunk_mfma.hip",
     "decode_kernel": "k_decode.hip",
@@ -252,6 +256,13 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     torch.cuda.synchronize()
     other_ms = t0.elapsed_time(t1) / steps
     del wso
+    # the fused schedule of the same call
+    wsf = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, chunk,
+                                         flags=msr.MSR_FLAG_FUSED), dtype=torch.uint8, device=dev)
+    ffn = lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=wsf, flags=msr.MSR_FLAG_FUSED)
+    ffn()
+    fused = stats_ms(per_call_ms(torch, ffn, steps))
+    del wsf
     kms = float(np.mean(kern_ms))
     flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     kflops = chunk_kernel_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
@@ -263,6 +274,7 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
         "kernel_tflops": kflops / (kms / 1e3) / 1e12, "step_tflops": flops / (ms / 1e3) / 1e12,
         "call": stats_ms(call_ms), "kernel": stats_ms(kern_ms), "flushed": flushed,
+        "fused": {**fused, "tokens_per_s": w.B * w.T / (fused["median_ms"] / 1e3)},
     }
 
 
@@ -295,6 +307,16 @@ def bench_long(torch, msr, mi, calls):
                               "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk) / (ms / 1e3) / 1e12,
                               "hbm_GBs": nbytes / (ms / 1e3) / 1e9,
                               "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        if chunk in (64, 128):  # the fused schedule at the same chunk
+            fl = msr.MSR_FLAG_FUSED
+            ws = torch.empty(msr.workspace_size(w.B, w.T, w.H, w.dk, w.dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE,
+                                                chunk, flags=fl), dtype=torch.uint8, device=dev)
+            fn = lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws, flags=fl)
+            fn()
+            st = stats_ms(per_call_ms(torch, fn, calls))
+            ms = st["median_ms"]
+            del ws
+            out["b%d" % chunk]["fused"] = {"ms_per_call": ms, **st, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
     return out
 
 
@@ -655,6 +677,7 @@ def main():
         "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",
                          "ms_per_step": r["split_scores_ms"]},
         "other_chunk": r["other_chunk"],
+        "fused_schedule": {"note": "the same call with MSR_FLAG_FUSED (opt-in schedule)", **r["fused"]},
         "long_sequence": lng,
         "cpu_baseline": cpu,
         "decode": dec,
