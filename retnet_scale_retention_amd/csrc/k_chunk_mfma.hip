@@ -156,6 +156,9 @@ struct Cfg {
     // it back from there
     static constexpr bool QSTAGE = 2 * BC * KROW + 2 * BC * 4 <= 163840;
     static constexpr int PREP_NT = QSTAGE && 2 * BC * KROW > 81920 ? 1024 : 512;
+    // prep_kernel's LDS tiles leave room for one workgroup per CU: its
+    // workgroups are then persistent (one per CU, several chunks each)
+    static constexpr bool PREP_PERSIST = (QSTAGE ? 2 : 1) * BC * KROW > 81920;
     static constexpr int VROW = W * 2;         // bytes per V row in LDS
     static constexpr int VTILE = BC * VROW;    // bytes of a chunk's V slice
     static constexpr int NV = VTILE / 1024 / NW;  // direct-load units per wave per chunk
@@ -251,10 +254,47 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     __shared__ __attribute__((aligned(16))) char Qs[QS ? BC * C::KROW : 16];  // Q~, the same layout
     __shared__ float dec[BC], zet[BC];  // s gamma^d, s gamma^(BC-1-t)
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l16 = lane & 15, g = lane >> 4;
     const int nch = c.T / BC;
-    const int pair = blockIdx.x / nch, ci = blockIdx.x % nch;
+    const int nblk = c.B * c.H * nch;  // (pair, chunk) blocks
+    const int ld = c.ldqk ? c.ldqk : DK;            // Q, K may be column slices of wider rows
+    const uint32_t rowQK = (uint32_t)c.H * ld * 2;  // bytes between tokens of Q, K
+    const bool rv = c.revqk != 0;
+    // byte offset of the chunk's row r from its first source token's row
+    auto roff = [&](int r) { return (uint32_t)(rv ? BC - 1 - r : r) * rowQK; };
+    // element offset of (pair, chunk) block blk's first source token row
+    auto block_base = [&](int blk) {
+        const int pr = blk / nch, cj = blk % nch;
+        const int tlo = rv ? c.T - (cj + 1) * BC : cj * BC;  // lowest source token of the chunk
+        return (((size_t)(pr / c.H) * c.T + (size_t)tlo) * c.H + pr % c.H) * ld;
+    };
+    // Workgroup w takes blocks w, w + gridDim.x, ...: one block each unless
+    // the tiles leave room for a single workgroup per CU (PREP_PERSIST), where
+    // the grid holds one workgroup per CU.  A thread holds its rotation rows
+    // of Q and K in registers; in a persistent workgroup, when they are few
+    // (PREFETCH), the next block's rows are loaded as soon as the current
+    // block's rotation has consumed them, so the loads overlap its fragment
+    // and score stage instead of following it.
+    constexpr bool PREFETCH = C::PREP_PERSIST && RPT <= 4;
+    const int c8 = (int)threadIdx.x % C8, r0 = ((int)threadIdx.x / C8) * RPT;
+    u32x4 xq[RPT], xk[RPT];
+    auto load_rows = [&](int blk) {
+        const char *qr = reinterpret_cast<const char *>(q + block_base(blk));
+        const char *kr = reinterpret_cast<const char *>(k + block_base(blk));
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            xq[j] = ld16(qr, roff(r0 + j) + c8 * 16);
+            xk[j] = ld16(kr, roff(r0 + j) + c8 * 16);
+        }
+    };
+  auto body = [&](int blk) __attribute__((always_inline)) {
+    if (!PREFETCH) load_rows(blk);
+    // (persistent: lane-dependent values are formed again from an opaque copy
+    // of the thread index in every block, rather than kept live across the loop)
+    int tid_r = threadIdx.x;
+    if constexpr (C::PREP_PERSIST) asm volatile("" : "+v"(tid_r));
+    const int tid = tid_r, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int pair = blk / nch, ci = blk % nch;
     const int b = pair / c.H, h = pair % c.H;
     const float lg = c.log2g[h];
     for (int t = tid; t < BC; t += NT) {
@@ -265,25 +305,10 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
             zet[t] = c.scale * exp2f((float)(BC - 1 - t - BC * (ci % rescale_period(lg, BC))) * lg);
     }
 
-    const int ld = c.ldqk ? c.ldqk : DK;            // Q, K may be column slices of wider rows
-    const uint32_t rowQK = (uint32_t)c.H * ld * 2;  // bytes between tokens of Q, K
-    const bool rv = c.revqk != 0;
-    const int tlo = rv ? c.T - (ci + 1) * BC : ci * BC;  // lowest source token of the chunk
-    const size_t base = (((size_t)b * c.T + (size_t)tlo) * c.H + h) * ld;
-    // byte offset of the chunk's row r from base
-    auto roff = [&](int r) { return (uint32_t)(rv ? BC - 1 - r : r) * rowQK; };
-    const char *qrow = reinterpret_cast<const char *>(q + base);
-    const char *krow = reinterpret_cast<const char *>(k + base);
+    const size_t base = block_base(blk);
 
-    uint16_t *qfo = qf + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG);
+    uint16_t *qfo = qf + (size_t)blk * (C::NKT * C::KS * FRAG);
     {  // ---- rotation: Q~ into LDS (or to its fragments), K~ into LDS
-        const int c8 = tid % C8, r0 = (tid / C8) * RPT;
-        u32x4 xq[RPT], xk[RPT];
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-            xq[j] = ld16(qrow, roff(r0 + j) + c8 * 16);
-            xk[j] = ld16(krow, roff(r0 + j) + c8 * 16);
-        }
         float cc[4] = {1.f, 1.f, 1.f, 1.f}, ss[4] = {0.f, 0.f, 0.f, 0.f}, c1[4], s1[4];
         const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
         if (rot) {
@@ -313,7 +338,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
                 *reinterpret_cast<u32x4 *>(Qs + C::koff(row, c8 * 8)) = rot ? yq : xq[j];
             else
                 *reinterpret_cast<u32x4 *>(qfo + fo) = rot ? yq : xq[j];
-            if (PAR) *reinterpret_cast<u32x4 *>(kq + (size_t)blockIdx.x * (C::NKT * C::KS * FRAG) + fo) = rot ? yk : xk[j];
+            if (PAR) *reinterpret_cast<u32x4 *>(kq + (size_t)blk * (C::NKT * C::KS * FRAG) + fo) = rot ? yk : xk[j];
             *reinterpret_cast<u32x4 *>(Ks + C::koff(row, c8 * 8)) = rot ? yk : xk[j];
             if (rot && j + 1 < RPT) {
 #pragma unroll
@@ -325,6 +350,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
             }
         }
     }
+    if (PREFETCH && blk + (int)gridDim.x < nblk) load_rows(blk + gridDim.x);
     __syncthreads();
 
     // ---- Q~ fragments from LDS, one whole fragment per store.  For the
@@ -359,7 +385,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     // K~[t][16 rt + n] s gamma^(BC-1-t) gamma^(-BC j) for t = 32 kb + 4 g + e
     // and t = 32 kb + 16 + 4 g + e (e = 0..3): the key order of the P^T
     // fragments, so that one transposed read of V serves both products
-    uint16_t *kfo = kf + (size_t)blockIdx.x * (C::RT * C::NB * FRAG) + lane * 8;
+    uint16_t *kfo = kf + (size_t)blk * (C::RT * C::NB * FRAG) + lane * 8;
     for (int f = w; f < C::RT * C::NB; f += PW) {
         const int rt = f / C::NB, kb = f % C::NB;
         const int row = 32 * kb + 4 * g + (l16 >> 2), col = 16 * rt + 4 * (l16 & 3);
@@ -376,11 +402,11 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     // ---- P^T = K~ Q~^T per 32-key block, masked, decayed, scaled; wave w
     // takes query tiles w and NKT - 1 - w (or w alone when NKT <= 8)
     constexpr int NU = C::NKT > PW ? 2 : 1;
-    if (PAR || w >= C::NKT) return;
+    if (!PAR && w < C::NKT) {
     int qt[NU];
     qt[0] = w;
     if (NU == 2) qt[NU - 1] = C::NKT - 1 - w;
-    uint16_t *pfo = pf + (size_t)blockIdx.x * (C::NKT * C::NB * FRAG) + lane * 8;
+    uint16_t *pfo = pf + (size_t)blk * (C::NKT * C::NB * FRAG) + lane * 8;
 #pragma unroll
     for (int kb = 0; kb < C::NB; ++kb) {
         bool nd[NU];
@@ -447,6 +473,15 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
                 }
             *reinterpret_cast<bf16x8 *>(pfo + (size_t)(qt[u] * C::NB + kb) * FRAG) = pb;
         }
+    }
+    }
+    if constexpr (C::PREP_PERSIST) __syncthreads();  // every wave is done with Ks, Qs, dec and zet of this block
+  };
+    if constexpr (C::PREP_PERSIST) {
+        if (PREFETCH && (int)blockIdx.x < nblk) load_rows(blockIdx.x);
+        for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) body(blk);
+    } else {
+        body(blockIdx.x);
     }
 }
 
@@ -1472,19 +1507,41 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(MsrConst c, int NS, co
     }
 }
 
+// Workgroups of the persistent kernel KERN (threads per workgroup given)
+// that the current device holds at once, at most nblk: its compute units
+// times the workgroups one unit keeps resident (cached per device).
+template <auto KERN>
+unsigned fill_grid(int threads, size_t nblk) {
+    static int resident[64];  // 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = resident[dev];
+    if (n == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, KERN, threads, 0) != hipSuccess || per <= 0) per = 1;
+        n = cus * per;
+        resident[dev] = n;
+    }
+    return (unsigned)(nblk < (size_t)n ? nblk : (size_t)n);
+}
+
 template <int DK, int BC, bool QPERM>
 void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, const void *Qlo,
                  const void *Klo, hipStream_t st) {
     using C = Cfg<DK, BC>;
-    const unsigned grid = (unsigned)(c.B * c.H * (c.T / BC));
+    const size_t nblk = (size_t)c.B * c.H * (c.T / BC);
     if (Qlo && Klo) {
-        auto pk = prep_kernel<DK, BC, false, true, QPERM>;
+        constexpr auto pk = prep_kernel<DK, BC, false, true, QPERM>;
+        const unsigned grid = C::PREP_PERSIST ? fill_grid<pk>(C::PREP_NT, nblk) : (unsigned)nblk;
         hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
                            static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo));
     } else {
-        auto pk = prep_kernel<DK, BC, false, false, QPERM>;
+        constexpr auto pk = prep_kernel<DK, BC, false, false, QPERM>;
+        const unsigned grid = C::PREP_PERSIST ? fill_grid<pk>(C::PREP_NT, nblk) : (unsigned)nblk;
         hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
@@ -1624,8 +1681,10 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     uint16_t *qf = reinterpret_cast<uint16_t *>(wsb + m.qf), *kq = reinterpret_cast<uint16_t *>(wsb + m.kq);
     uint16_t *kf = reinterpret_cast<uint16_t *>(wsb + m.kf);
     float2 *stats = NSO > 1 ? reinterpret_cast<float2 *>(wsb + m.stats) : nullptr;
-    auto pk = prep_kernel<DK, 64, true>;
-    hipLaunchKernelGGL(pk, dim3(npairs * nqb), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
+    constexpr auto pk = prep_kernel<DK, 64, true>;
+    const size_t pblk = (size_t)npairs * nqb;
+    const unsigned pgrid = Cfg<DK, 64>::PREP_PERSIST ? fill_grid<pk>(Cfg<DK, 64>::PREP_NT, pblk) : (unsigned)pblk;
+    hipLaunchKernelGGL(pk, dim3(pgrid), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq, (const uint16_t *)nullptr,
                        (const uint16_t *)nullptr);
     hipError_t e = hipGetLastError();
