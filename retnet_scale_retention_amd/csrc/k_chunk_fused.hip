@@ -202,15 +202,16 @@ __device__ __forceinline__ void static_for(F &&f) {
 // angle in quarter turns, pos * t4, is reduced to the nearest whole number q
 // plus a remainder in [-1/2, 1/2] (exact: the subtraction of q loses no
 // bits), i.e. y in [-pi/4, pi/4] radians; sin and cos of y come from their
-// Taylor series up to y^9 and y^8 (truncation below 2e-9), and q mod 4
-// quarter turns then rotate the pair.
+// Taylor series up to y^9 and y^10 (truncation below 2e-9 and 1.2e-10), and
+// q mod 4 quarter turns then rotate the pair.
 __device__ __forceinline__ void rot_cs(double pos, double t4, float &cs, float &sn) {
     const double qt = pos * t4;
     const double q = rint(qt);
     const float y = (float)(qt - q) * 1.57079633f;
     const float y2 = y * y;
     const float s = y * (1.f - y2 * (1.f / 6.f - y2 * (1.f / 120.f - y2 * (1.f / 5040.f - y2 * (1.f / 362880.f)))));
-    const float c = 1.f - y2 * (0.5f - y2 * (1.f / 24.f - y2 * (1.f / 720.f - y2 * (1.f / 40320.f))));
+    const float c =
+        1.f - y2 * (0.5f - y2 * (1.f / 24.f - y2 * (1.f / 720.f - y2 * (1.f / 40320.f - y2 * (1.f / 3628800.f)))));
     // quarter turns: (c, s) -> (-s, c) -> (-c, -s) -> (s, -c), without branches
     const int qq = (int)(q - 4.0 * floor(q * 0.25));
     const float a = (qq & 1) ? s : c, bb = (qq & 1) ? c : s;

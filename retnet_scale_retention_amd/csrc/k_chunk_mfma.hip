@@ -211,7 +211,7 @@ struct Cfg {
 //
 // Rotation: thread (c8, rg) handles channels 8 c8 .. 8 c8 + 7 (4 pairs) of a
 // run of RPT consecutive rows.  The angles of the run's first row come from
-// rot_cos_sin (fp64 reduction); each next row multiplies (cos, sin) by
+// rot_cos_sin (fp64 quarter-turn reduction); each next row multiplies (cos, sin) by
 // (cos theta_i, sin theta_i) -- the angle-addition formula, a few ulp of
 // drift over at most 16 rows.  Q~ goes straight to its fragments in global
 // memory, K~ of the chunk to LDS; the score products read Q~ back from the
@@ -253,6 +253,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     __shared__ __attribute__((aligned(16))) char Ks[BC * C::KROW];            // K~, swizzled rows
     __shared__ __attribute__((aligned(16))) char Qs[QS ? BC * C::KROW : 16];  // Q~, the same layout
     __shared__ float dec[BC], zet[BC];  // s gamma^d, s gamma^(BC-1-t)
+    __shared__ float2 step[DK / 2];     // cos and sin of theta_i: the angle step from row to row
 
     const int nch = c.T / BC;
     const int nblk = c.B * c.H * nch;  // (pair, chunk) blocks
@@ -286,6 +287,15 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
             xk[j] = ld16(kr, roff(r0 + j) + c8 * 16);
         }
     };
+    const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
+    if (rot) {
+        for (int i = threadIdx.x; i < DK / 2; i += NT) {
+            float cs, sn;
+            rot_cos_sin(1, c.theta[i], cs, sn);
+            step[i] = float2{cs, sn};
+        }
+    }
+    __syncthreads();
   auto body = [&](int blk) __attribute__((always_inline)) {
     if (!PREFETCH) load_rows(blk);
     // (persistent: lane-dependent values are formed again from an opaque copy
@@ -310,14 +320,14 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     uint16_t *qfo = qf + (size_t)blk * (C::NKT * C::KS * FRAG);
     {  // ---- rotation: Q~ into LDS (or to its fragments), K~ into LDS
         float cc[4] = {1.f, 1.f, 1.f, 1.f}, ss[4] = {0.f, 0.f, 0.f, 0.f}, c1[4], s1[4];
-        const bool rot = !(c.flags & MSR_FLAG_NO_ROTATE);
         if (rot) {
             const int64_t p0 = row_pos0(c, b) + (int64_t)ci * BC + r0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float th = c.theta[4 * c8 + i];
-                rot_cos_sin(p0, th, cc[i], ss[i]);
-                rot_cos_sin(1, th, c1[i], s1[i]);
+                rot_cos_sin(p0, c.theta[4 * c8 + i], cc[i], ss[i]);
+                const float2 st = step[4 * c8 + i];
+                c1[i] = st.x;
+                s1[i] = st.y;
             }
         }
 #pragma unroll

@@ -29,19 +29,27 @@ __device__ __forceinline__ void store(float *p, size_t i, float x) { p[i] = x; }
 __device__ __forceinline__ void store(uint16_t *p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 
 // ---- rotation angle ---------------------------------------------------------
-// cos/sin of pos * theta.  The product and the reduction modulo 2*pi are done
-// in fp64 (pos reaches 1e5 and more, where an fp32 product would already be
-// off by ~1e-2 rad); the reduced angle in [-pi, pi] is then evaluated in fp32.
-// 2*pi is split in two doubles (Cody and Waite's argument reduction).
+// cos and sin of the rotation angle pos * theta.  The angle in quarter
+// turns, pos * theta * 2/pi, is formed in fp64 (pos reaches 1e5 and more,
+// where an fp32 product would already be off by ~1e-2 rad) and split into
+// the nearest whole number q and a remainder in [-1/2, 1/2] (exact: the
+// subtraction of q loses no bits); sin and cos of the remainder
+// y in [-pi/4, pi/4] radians come from their Taylor series up to y^9 and
+// y^10 (truncation below 2e-9 and 1.2e-10), and q mod 4 quarter turns then
+// rotate the pair.
 __device__ __forceinline__ void rot_cos_sin(int64_t pos, float theta, float &cs, float &sn) {
-    const double two_pi_hi = 6.283185307179586;       // nearest double to 2*pi
-    const double two_pi_lo = 2.4492935982947064e-16;  // 2*pi - two_pi_hi
-    const double inv_two_pi = 0.15915494309189535;
-    double phi = static_cast<double>(pos) * static_cast<double>(theta);
-    double k = rint(phi * inv_two_pi);
-    double r = fma(-k, two_pi_hi, phi);
-    r = fma(-k, two_pi_lo, r);
-    sincosf(static_cast<float>(r), &sn, &cs);
+    const double qt = static_cast<double>(pos) * (static_cast<double>(theta) * 0.63661977236758134);  // 2 / pi
+    const double q = rint(qt);
+    const float y = static_cast<float>(qt - q) * 1.57079633f;
+    const float y2 = y * y;
+    const float s = y * (1.f - y2 * (1.f / 6.f - y2 * (1.f / 120.f - y2 * (1.f / 5040.f - y2 * (1.f / 362880.f)))));
+    const float c =
+        1.f - y2 * (0.5f - y2 * (1.f / 24.f - y2 * (1.f / 720.f - y2 * (1.f / 40320.f - y2 * (1.f / 3628800.f)))));
+    // (c, s) turned by qq quarter turns: (c, s), (-s, c), (-c, -s), (s, -c)
+    const int qq = static_cast<int>(q - 4.0 * floor(q * 0.25));
+    const float a = (qq & 1) ? s : c, b = (qq & 1) ? c : s;
+    cs = (qq == 1 || qq == 2) ? -a : a;
+    sn = (qq >= 2) ? -b : b;
 }
 
 // position of token 0 of batch row b

@@ -207,3 +207,34 @@ def test_small_layer_chunkwise_and_parallel():
     o2, st2 = run_gpu("parallel", q, k, v, g, "bf16")
     assert out_err(o2, ro) < TOL["bf16"] and state_err(st2, rs) < TOL["bf16"]
     assert out_err(o2, o) < TOL["bf16"]
+
+
+# ------------------------------------------- rotation at large positions
+BIG_POS = 3_000_000_017  # angles of 3e9 rad and more: the fp64 angle reduction
+
+
+@pytest.mark.parametrize("route", ["mfma-chunk", "mfma-parallel", "generic-fp32", "steps-fp32", "steps-bf16"])
+def test_large_start_position(route):
+    """Every rotating kernel at a start position near 3e9 (explicit fp32 theta on
+    both sides, so that both rotate by the same frequencies)."""
+    dtype = "f32" if route.endswith("fp32") else "bf16"
+    dk, dv = (256, 256) if route.startswith("mfma") else (32, 32)
+    T = 256 if route.startswith("mfma") else 24
+    w = mi.Workload("bigpos", 71, 1, T, 2, dk, dv, dtype, (128,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = mi.gammas(2)
+    th = orc.default_theta(dk)
+    if route == "mfma-parallel":
+        ro, rs = orc.parallel(q, k, v, g, s_in=s, pos0=BIG_POS, theta=th)
+        o, st = run_gpu("parallel", q, k, v, g, dtype, s_in=s, pos0=BIG_POS, theta=th)
+    elif route.startswith("steps"):
+        ro, rs = orc.recurrent(q, k, v, g, s_in=s, pos0=BIG_POS, theta=th)
+        o, st = run_steps(q, k, v, g, dtype, s, BIG_POS, theta=th)
+    else:
+        chunk = 128 if route == "mfma-chunk" else 8
+        ro, rs = orc.recurrent(q, k, v, g, s_in=s, pos0=BIG_POS, theta=th)
+        o, st = run_gpu("chunk", q, k, v, g, dtype, chunk=chunk, s_in=s, pos0=BIG_POS, theta=th)
+    eo, es = out_err(o, ro), state_err(st, rs)
+    note(f"{route} pos0 {BIG_POS}: O err {eo:.2e}  state err {es:.2e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
