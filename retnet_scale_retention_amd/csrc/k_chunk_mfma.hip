@@ -409,81 +409,59 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
         *reinterpret_cast<bf16x8 *>(kfo + (size_t)f * FRAG) = x;
     }
 
-    // ---- P^T = K~ Q~^T per 32-key block, masked, decayed, scaled; wave w
-    // takes query tiles w and NKT - 1 - w (or w alone when NKT <= 8)
-    constexpr int NU = C::NKT > PW ? 2 : 1;
-    if (!PAR && w < C::NKT) {
-    int qt[NU];
-    qt[0] = w;
-    if (NU == 2) qt[NU - 1] = C::NKT - 1 - w;
-    uint16_t *pfo = pf + (size_t)blk * (C::NKT * C::NB * FRAG) + lane * 8;
+    // ---- P^T = K~ Q~^T for every (query tile u, 32-key block kb) the tile
+    // reaches (32 kb <= 16 u + 15, i.e. kb <= u / 2), masked, decayed and
+    // scaled.  The items, in (u, kb) order, are dealt to all the waves in turn
+    // (at most two per wave at the 7B shape's 20 items and 16 waves).
+    if (!PAR) {
+        constexpr int NI = [] {
+            int n = 0;
+            for (int u = 0; u < C::NKT; ++u) n += u / 2 + 1;
+            return n;
+        }();
+        uint16_t *pfo = pf + (size_t)blk * (C::NKT * C::NB * FRAG) + lane * 8;
+        for (int it = w; it < NI; it += PW) {
+            int u = 0, kb = it;  // (uniform)
+            while (kb > u / 2) {
+                kb -= u / 2 + 1;
+                ++u;
+            }
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int kb = 0; kb < C::NB; ++kb) {
-        bool nd[NU];
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            nd[u] = 32 * kb <= 16 * qt[u] + 15;
-            any = any || nd[u];
-        }
-        if (!any) continue;
-        f32x4 acc[NU][2];
-#pragma unroll
-        for (int u = 0; u < NU; ++u) acc[u][0] = acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            bf16x8 ka[2], qb[NU];
-#pragma unroll
-            for (int v2 = 0; v2 < 2; ++v2)
-                ka[v2] = *reinterpret_cast<const bf16x8 *>(Ks + C::koff(32 * kb + 16 * v2 + l16, 32 * ks + 8 * g));
-#pragma unroll
-            for (int u = 0; u < NU; ++u)
-                qb[u] = QS ? __builtin_bit_cast(bf16x8, ld16(Qs, C::koff(16 * qt[u] + l16, 32 * ks + 8 * g)))
-                           : ldf(qfo + (size_t)(qt[u] * C::KS + ks) * FRAG + lane * 8);
-#pragma unroll
-            for (int u = 0; u < NU; ++u)
-                if (nd[u]) {
-#pragma unroll
-                    for (int v2 = 0; v2 < 2; ++v2) acc[u][v2] = mfma16(ka[v2], qb[u], acc[u][v2]);
-                }
-            if constexpr (SPLIT) {
-                const char *ql = reinterpret_cast<const char *>(qlo + base);
-                const char *kl = reinterpret_cast<const char *>(klo + base);
-                bf16x8 kla[2], qlb[NU];
+            for (int ks = 0; ks < C::KS; ++ks) {
+                bf16x8 ka[2];
 #pragma unroll
                 for (int v2 = 0; v2 < 2; ++v2)
-                    kla[v2] = __builtin_bit_cast(bf16x8, ld16(kl, roff(32 * kb + 16 * v2 + l16) +
-                                                                      (32 * ks + 8 * g) * 2));
+                    ka[v2] = *reinterpret_cast<const bf16x8 *>(Ks + C::koff(32 * kb + 16 * v2 + l16, 32 * ks + 8 * g));
+                const bf16x8 qb = QS ? __builtin_bit_cast(bf16x8, ld16(Qs, C::koff(16 * u + l16, 32 * ks + 8 * g)))
+                                     : ldf(qfo + (size_t)(u * C::KS + ks) * FRAG + lane * 8);
 #pragma unroll
-                for (int u = 0; u < NU; ++u)
-                    qlb[u] = __builtin_bit_cast(bf16x8, ld16(ql, roff(16 * qt[u] + l16) +
-                                                                 (32 * ks + 8 * g) * 2));
+                for (int v2 = 0; v2 < 2; ++v2) acc[v2] = mfma16(ka[v2], qb, acc[v2]);
+                if constexpr (SPLIT) {
+                    const char *ql = reinterpret_cast<const char *>(qlo + base);
+                    const char *kl = reinterpret_cast<const char *>(klo + base);
+                    const bf16x8 qlb =
+                        __builtin_bit_cast(bf16x8, ld16(ql, roff(16 * u + l16) + (32 * ks + 8 * g) * 2));
 #pragma unroll
-                for (int u = 0; u < NU; ++u)
-                    if (nd[u]) {
-#pragma unroll
-                        for (int v2 = 0; v2 < 2; ++v2) {
-                            acc[u][v2] = mfma16(kla[v2], qb[u], acc[u][v2]);
-                            acc[u][v2] = mfma16(ka[v2], qlb[u], acc[u][v2]);
-                        }
+                    for (int v2 = 0; v2 < 2; ++v2) {
+                        const bf16x8 kla = __builtin_bit_cast(
+                            bf16x8, ld16(kl, roff(32 * kb + 16 * v2 + l16) + (32 * ks + 8 * g) * 2));
+                        acc[v2] = mfma16(kla, qb, acc[v2]);
+                        acc[v2] = mfma16(ka[v2], qlb, acc[v2]);
                     }
+                }
             }
-        }
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            if (!nd[u]) continue;
-            const int jq = 16 * qt[u] + l16;
+            const int jq = 16 * u + l16;
             bf16x8 pb;
 #pragma unroll
             for (int v2 = 0; v2 < 2; ++v2)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 32 * kb + 16 * v2 + 4 * g + r;
-                    pb[4 * v2 + r] = static_cast<__bf16>((t <= jq) ? acc[u][v2][r] * dec[jq - t] : 0.f);
+                    pb[4 * v2 + r] = static_cast<__bf16>((t <= jq) ? acc[v2][r] * dec[jq - t] : 0.f);
                 }
-            *reinterpret_cast<bf16x8 *>(pfo + (size_t)(qt[u] * C::NB + kb) * FRAG) = pb;
+            *reinterpret_cast<bf16x8 *>(pfo + (size_t)(u * C::NB + kb) * FRAG) = pb;
         }
-    }
     }
     if constexpr (C::PREP_PERSIST) __syncthreads();  // every wave is done with Ks, Qs, dec and zet of this block
   };
