@@ -1269,20 +1269,20 @@ struct ParArgs {
     int NS;
 };
 
-template <int DK, int PW>
+template <int DK, int PW, int NQW>
 __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs a) {
     using C = Cfg<DK, 64>;
     constexpr int KS = DK / 32;
     constexpr int CT = PW / 16;            // 16-column tiles of the slice
+    constexpr int QB = 64 * NQW;           // queries per workgroup
     constexpr int KBYTES = 2 * KS * 1024;  // K~ fragments of one 32-key block
     constexpr int VBYTES = 32 * PW * 2;    // V slice of one 32-key block
     constexpr int NVL = VBYTES / 1024 / 4; // 1 KiB direct loads of it per wave
-    static_assert(PW % 64 == 0 && NVL >= 1, "slice width");
+    static_assert(PW % 64 == 0 && NVL >= 1 && (NQW == 1 || NQW == 2), "slice width, query tiles per wave");
     // V rows (PW 2 bytes) with their 16-byte chunks XOR-swizzled by row so
     // that the transpose reads of a 16-lane group (4 rows x 32 bytes) spread
     // over the banks
     auto vswz = [](int r) { return PW == 64 ? (r >> 1) & 7 : ((r & 3) << 1) | ((r >> 2) & 1); };
-    auto voffp = [&](int r, int col) { return r * (PW * 2) + ((((col >> 3) ^ vswz(r))) << 4) + (col & 7) * 2; };
     // K~ and V double buffers; before the first block the same LDS holds
     // S_in^T, 64 columns at a time (so that two workgroups fit on a CU)
     __shared__ __attribute__((aligned(16))) char L[2 * KBYTES + 2 * VBYTES];
@@ -1292,16 +1292,42 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int nqb = c.T / 64;
-    const int slice = blockIdx.x % a.NS, qb = (blockIdx.x / a.NS) % nqb, pair = blockIdx.x / a.NS / nqb;
+    const int nqb = c.T / QB;
+    // workgroup -> (pair, query block, slice).  Query block qb takes qb + 1
+    // key-block units of work, so the workgroups are dispatched latest query
+    // block first (the short ones fill the end); with pairs a multiple of 8,
+    // the workgroups of one pair get ids equal mod 8 and run on one XCD,
+    // whose L2 then serves its K~ and V blocks to all of them.
+    int slice, qb, pair;
+    {
+        const int id = blockIdx.x, npairs = c.B * c.H;
+        if (npairs % 8 == 0) {
+            const int xcd = id & 7, j = id >> 3, pl = npairs / 8;
+            slice = j % a.NS;
+            const int pq = j / a.NS;
+            pair = (pq % pl) * 8 + xcd;
+            qb = nqb - 1 - pq / pl;
+        } else {
+            slice = id % a.NS;
+            pair = (id / a.NS) % npairs;
+            qb = nqb - 1 - id / a.NS / npairs;
+        }
+    }
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * PW;
     const float lg = c.log2g[h];
-    const int tile = 4 * qb + w;              // this wave's query tile
-    const int n = 16 * tile + l16;            // this lane's query row (as MFMA column)
+    // this wave's query tiles: 4 qb + w, or with two per wave 8 qb + w and
+    // 8 qb + 7 - w (equal causal work across the waves)
+    int tile[NQW], n[NQW];
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+        tile[i] = i == 0 ? 4 * NQW * qb + w : 8 * qb + 7 - w;
+        n[i] = 16 * tile[i] + l16;  // this lane's query row (as MFMA column)
+    }
     const uint32_t loff = lane * 16;
-    const uint16_t *qfb = a.qf + (size_t)pair * nqb * (4 * KS * FRAG);
-    const uint16_t *kqb = a.kq + (size_t)pair * nqb * (4 * KS * FRAG);
+    // (Q~ and K~ fragments in prep_kernel's blocks of 64 queries)
+    const uint16_t *qfb = a.qf + (size_t)pair * (c.T / 64) * (4 * KS * FRAG);
+    const uint16_t *kqb = a.kq + (size_t)pair * (c.T / 64) * (4 * KS * FRAG);
     const uint32_t rowV = (uint32_t)c.H * c.dv * 2;
     const char *vb = reinterpret_cast<const char *>(a.v + ((size_t)b * c.T * c.H + h) * c.dv + col0);
 
@@ -1318,15 +1344,19 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
         }
     };
 
-    bf16x8 qr[KS];
+    bf16x8 qr[NQW][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qr[ks] = *reinterpret_cast<const bf16x8 *>(
-            reinterpret_cast<const char *>(qfb + (size_t)(tile * KS + ks) * FRAG) + loff);
+    for (int i = 0; i < NQW; ++i)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qr[i][ks] = *reinterpret_cast<const bf16x8 *>(
+                reinterpret_cast<const char *>(qfb + (size_t)(tile[i] * KS + ks) * FRAG) + loff);
 
-    f32x4 oacc[CT];
+    f32x4 oacc[NQW][CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NQW; ++i)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) oacc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.s_in) {  // (S_in^T Q~^T) gamma^(n+1), 64 value columns at a time
 #pragma unroll
         for (int sc = 0; sc < PW / W; ++sc) {
@@ -1340,45 +1370,104 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int t = 0; t < W / 16; ++t)
-                    oacc[sc * (W / 16) + t] = mfma16(
-                        *reinterpret_cast<const bf16x8 *>(St + (t * 16 + l16) * C::SP + 32 * ks + 8 * g), qr[ks],
-                        oacc[sc * (W / 16) + t]);
-        }
-        const float x = exp2f((float)(n + 1) * lg);
+                for (int t = 0; t < W / 16; ++t) {
+                    const bf16x8 A = *reinterpret_cast<const bf16x8 *>(St + (t * 16 + l16) * C::SP + 32 * ks + 8 * g);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) oacc[ct] = oacc[ct] * x;
+                    for (int i = 0; i < NQW; ++i)
+                        oacc[i][sc * (W / 16) + t] = mfma16(A, qr[i][ks], oacc[i][sc * (W / 16) + t]);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+            const float x = exp2f((float)(n[i] + 1) * lg);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) oacc[i][ct] = oacc[i][ct] * x;
+        }
         __syncthreads();  // every wave is done with S_in^T before the loads overwrite it
     }
 
-    const int nkb = 2 * qb + 2;  // key blocks up to the block's last query
+    // Decay of score (query n, key m = 32 kb + o), o = 16 v2 + 4 g + r the key
+    // offset this lane holds:
+    //   s gamma^(n - m) = [s gamma^(n - 32 kb - 31) gamma^(31 - 4 g)] gamma^(-(16 v2 + r)),
+    // one exponential per tile and block times a lane factor, times one of
+    // eight wave-uniform factors (gamma >= 0.9 on this path: every factor
+    // stays below gamma^-31 < 27, and their product is gamma^(n - m) <= 1)
+    const float dg = exp2f((float)(31 - 4 * g) * lg);
+    float du[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        du[e] = __uint_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_uint(exp2f(-(float)(16 * (e >> 2) + (e & 3)) * lg))));
+
+    // V^T transpose-read addresses: lane rows rv and rv + 16, columns
+    // 16 ct + 4 (l16 & 3); the 16-byte chunk 2 ct + b of the row is stored at
+    // (2 ct + b) ^ sw = 2 (ct ^ (sw >> 1)) + (b ^ (sw & 1)), and sw >> 1 < 4 only
+    // changes the low two bits of ct: four lane bases cover every ct, the rest
+    // is an immediate offset
+    const int rv = 4 * g + (l16 >> 2), sv = vswz(rv);  // (vswz(rv + 16) = vswz(rv))
+    uint32_t vl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        vl[k] = rv * (PW * 2) + 32 * (k ^ (sv >> 1)) + 16 * (((l16 & 3) >> 1) ^ (sv & 1)) + 8 * (l16 & 1);
+
+    const int nkb = (QB / 32) * (qb + 1);  // key blocks up to the workgroup's last query
     dma(0, Kb0, Vb0);
     auto block = [&](int kb, const char *Kc, const char *Vc, char *Kn, char *Vn) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kb + 1 < nkb) dma(kb + 1, Kn, Vn);
-        if (32 * kb > n - l16 + 15) return;  // the whole tile is before this block
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bool act[NQW];  // the tile reaches this block (uniform)
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+            act[i] = 32 * kb <= 16 * tile[i] + 15;
+            any = any || act[i];
+        }
+        if (!any) return;
+        f32x4 acc[NQW][2];
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int v2 = 0; v2 < 2; ++v2)
-                acc[v2] = mfma16(*reinterpret_cast<const bf16x8 *>(Kc + (v2 * KS + ks) * 1024 + loff), qr[ks], acc[v2]);
-        bf16x8 pb;
+            for (int v2 = 0; v2 < 2; ++v2) {
+                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(Kc + (v2 * KS + ks) * 1024 + loff);
 #pragma unroll
-        for (int v2 = 0; v2 < 2; ++v2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 32 * kb + 16 * v2 + 4 * g + r;
-                pb[4 * v2 + r] =
-                    static_cast<__bf16>(m <= n ? acc[v2][r] * c.scale * exp2f((float)(n - m) * lg) : 0.f);
+                for (int i = 0; i < NQW; ++i)
+                    if (act[i]) acc[i][v2] = mfma16(A, qr[i][ks], acc[i][v2]);
             }
+        bf16x8 pb[NQW];
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+            if (!act[i]) continue;
+            const float base = c.scale * exp2f((float)(n[i] - 32 * kb - 31) * lg) * dg;
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = base * du[e];
+            if (32 * kb + 31 <= 16 * tile[i]) {  // (uniform) every key before every query of the tile
+#pragma unroll
+                for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pb[i][4 * v2 + r] = static_cast<__bf16>(acc[i][v2][r] * f[4 * v2 + r]);
+            } else {
+#pragma unroll
+                for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 32 * kb + 16 * v2 + 4 * g + r;
+                        pb[i][4 * v2 + r] = static_cast<__bf16>(m <= n[i] ? acc[i][v2][r] * f[4 * v2 + r] : 0.f);
+                    }
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int col = ct * 16 + 4 * (l16 & 3);
-            const s16x4 v0 = lds_tr(Vc + voffp(4 * g + (l16 >> 2), col));
-            const s16x4 v1 = lds_tr(Vc + voffp(16 + 4 * g + (l16 >> 2), col));
-            oacc[ct] = mfma16(cat(v0, v1), pb, oacc[ct]);
+            const char *va = Vc + vl[ct & 3] + 128 * (ct >> 2);
+            const s16x4 v0 = lds_tr(va);
+            const s16x4 v1 = lds_tr(va + 16 * PW * 2);
+            const bf16x8 Vf = cat(v0, v1);
+#pragma unroll
+            for (int i = 0; i < NQW; ++i)
+                if (act[i]) oacc[i][ct] = mfma16(Vf, pb[i], oacc[i][ct]);
         }
     };
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -1389,38 +1478,41 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     // GroupNorm (in-wave when d_v == 64, else slice statistics) and store
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
-    const uint32_t rowi = (uint32_t)n * c.H + h;  // token-head row within the batch row
-    if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
-        const float f = 1.f / decay_row_sum(row_pos0(c, b) + n, lg);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) oacc[ct] = oacc[ct] * f;
-    }
-    if (norm_here || stats_out) {
-        float sum = 0.f;
+    for (int i = 0; i < NQW; ++i) {
+        const uint32_t rowi = (uint32_t)n[i] * c.H + h;  // token-head row within the batch row
+        if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
+            const float f = 1.f / decay_row_sum(row_pos0(c, b) + n[i], lg);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) sum += oacc[ct][0] + oacc[ct][1] + oacc[ct][2] + oacc[ct][3];
-        const float mean = sum_lane_groups(sum) * (1.f / PW);
-        float m2 = 0.f;
+            for (int ct = 0; ct < CT; ++ct) oacc[i][ct] = oacc[i][ct] * f;
+        }
+        if (norm_here || stats_out) {
+            float sum = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m2 += (oacc[ct][r] - mean) * (oacc[ct][r] - mean);
-        m2 = sum_lane_groups(m2);
-        if (stats_out && g == 0)
-            a.stats[((size_t)b * c.T * c.H + rowi) * a.NS + slice] = make_float2(mean, m2);
-        if (norm_here) {
-            const float inv = 1.f / sqrtf(m2 * (1.f / PW) + c.eps);
+            for (int ct = 0; ct < CT; ++ct) sum += oacc[i][ct][0] + oacc[i][ct][1] + oacc[i][ct][2] + oacc[i][ct][3];
+            const float mean = sum_lane_groups(sum) * (1.f / PW);
+            float m2 = 0.f;
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[ct][r] = (oacc[ct][r] - mean) * inv;
-        }
-    }
-    uint16_t *dst = a.o + ((size_t)b * c.T * c.H + rowi) * c.dv + col0 + 4 * g;
+                for (int r = 0; r < 4; ++r) m2 += (oacc[i][ct][r] - mean) * (oacc[i][ct][r] - mean);
+            m2 = sum_lane_groups(m2);
+            if (stats_out && g == 0)
+                a.stats[((size_t)b * c.T * c.H + rowi) * a.NS + slice] = make_float2(mean, m2);
+            if (norm_here) {
+                const float inv = 1.f / sqrtf(m2 * (1.f / PW) + c.eps);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        const u32x2 v2 = {pack_bf16x2(oacc[ct][0], oacc[ct][1]), pack_bf16x2(oacc[ct][2], oacc[ct][3])};
-        *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) oacc[i][ct][r] = (oacc[i][ct][r] - mean) * inv;
+            }
+        }
+        uint16_t *dst = a.o + ((size_t)b * c.T * c.H + rowi) * c.dv + col0 + 4 * g;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const u32x2 v2 = {pack_bf16x2(oacc[i][ct][0], oacc[i][ct][1]), pack_bf16x2(oacc[i][ct][2], oacc[i][ct][3])};
+            *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+        }
     }
 }
 
@@ -1679,8 +1771,12 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     if (e != hipSuccess) return e;
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
     main_kernel_begin(st);
-    auto ok = PW == 256 ? parallel_mfma_kernel<DK, 256> : parallel_mfma_kernel<DK, 64>;
-    hipLaunchKernelGGL(ok, dim3(npairs * nqb * NSO), dim3(256), 0, st, c, pa);
+    // two query tiles per wave (128 queries per workgroup) when T allows: each
+    // K~ and V fragment read from LDS then serves two MFMAs
+    const int nq2 = c.T % 128 == 0 ? 2 : 1;
+    auto ok = PW == 256 ? (nq2 == 2 ? parallel_mfma_kernel<DK, 256, 2> : parallel_mfma_kernel<DK, 256, 1>)
+                        : (nq2 == 2 ? parallel_mfma_kernel<DK, 64, 2> : parallel_mfma_kernel<DK, 64, 1>);
+    hipLaunchKernelGGL(ok, dim3(npairs * (c.T / (64 * nq2)) * NSO), dim3(256), 0, st, c, pa);
     e = hipGetLastError();
     main_kernel_end(st);
     if (e != hipSuccess) return e;
