@@ -499,8 +499,7 @@ __global__ __launch_bounds__(NTH) void chunk_fused_kernel(MsrConst c, FusedArgs 
     // ---- state -------------------------------------------------------------
     f32x4 S[C::RT][CT];
     {
-        const float gseg = exp2f((float)(BC * a.seglen) * lg);  // gamma^(b seglen)
-        const float f0 = 1.f;                                   // runs start from the true state
+        const float gseg = exp2f((float)(BC * a.seglen) * lg);  // gamma^(b seglen); runs start from the true state
         const float *sin_p = a.nseg > 1 ? a.segE + ebase + (size_t)(a.nseg - 1) * estride
                                         : (a.s_in ? a.s_in + pstate : nullptr);
 #pragma unroll
@@ -515,7 +514,7 @@ __global__ __launch_bounds__(NTH) void chunk_fused_kernel(MsrConst c, FusedArgs 
                         x = sin_p ? sin_p[o] : 0.f;
                         for (int gg = 0; gg < seg; ++gg) x = x * gseg + a.segE[ebase + gg * estride + o];
                     }
-                    S[rt][ct][r] = x * f0;
+                    S[rt][ct][r] = x;
                 }
     }
 
@@ -926,6 +925,8 @@ bool chunk_fused_supported(int dk, int dv, int bc) {
 
 hipError_t launch_chunk_fused(const MsrConst &c, const FusedArgs &a, int bc, bool state_only, hipStream_t st) {
     if (state_only && (a.nseg < 2 || !a.segE)) return hipErrorInvalidValue;
+    // (the kernel applies no row-normalised decay: such calls take the default schedule)
+    if (c.flags & MSR_FLAG_DECAY_ROWNORM) return hipErrorInvalidValue;
     switch (c.dk * 1000 + bc) {
     case 128064: return launch_dk_bc<128, 64>(c, a, state_only, st);
     case 128128: return launch_dk_bc<128, 128>(c, a, state_only, st);

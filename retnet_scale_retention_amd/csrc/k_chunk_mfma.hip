@@ -6,10 +6,11 @@
 //   S_i = gamma^b S_{i-1} + K~_i^T (V_i (.) zeta)
 //
 // Kernels, in launch order:
-//   prep_kernel         per (pair, chunk), fully parallel: rotates the chunk's
-//                       Q and K rows, computes its masked, decayed scores
-//                       P = (Q~ K~^T (.) D) s, and writes Q~, K~^T and P^T as
-//                       MFMA operand fragments
+//   prep_kernel         per (pair, chunk), fully parallel (persistent
+//                       workgroups, one per CU, where its tiles fill the
+//                       LDS): rotates the chunk's Q and K rows, computes its
+//                       masked, decayed scores P = (Q~ K~^T (.) D) s, and
+//                       writes Q~, K~^T and P^T as MFMA operand fragments
 //   chunk_mfma_kernel   the recurrence over the chunks, below
 //   gn_finalize_kernel  GroupNorm when d_v spans several slices
 //
