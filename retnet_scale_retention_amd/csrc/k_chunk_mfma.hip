@@ -11,8 +11,11 @@
 //                       LDS): rotates the chunk's Q and K rows, computes its
 //                       masked, decayed scores P = (Q~ K~^T (.) D) s, and
 //                       writes Q~, K~^T and P^T as MFMA operand fragments
-//   chunk_mfma_kernel   the recurrence over the chunks, below
-//   gn_finalize_kernel  GroupNorm when d_v spans several slices
+//   chunk_mfma_kernel   the recurrence over the chunks, below (b <= 128:
+//   / chunk_ws_kernel   its warp-specialised variant, which normalises rows
+//                       spanning 2 to 8 slices itself by exchanging slice
+//                       statistics between the slices' workgroups)
+//   gn_finalize_kernel  GroupNorm when d_v spans several slices otherwise
 //
 // Fragments.  A 16x16x32 MFMA operand is 64 lanes x 8 bf16: lane 16 g + n
 // holds row n, k-indices 8 g .. 8 g + 7.  prep_kernel stores each operand the
@@ -241,7 +244,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
                                                                   uint16_t *__restrict__ qf, uint16_t *__restrict__ kf,
                                                                   uint16_t *__restrict__ pf, uint16_t *__restrict__ kq,
                                                                   const uint16_t *__restrict__ qlo = nullptr,
-                                                                  const uint16_t *__restrict__ klo = nullptr) {
+                                                                  const uint16_t *__restrict__ klo = nullptr,
+                                                                  unsigned long long *__restrict__ xz = nullptr,
+                                                                  int xns = 0, unsigned *__restrict__ xtick = nullptr) {
     using C = Cfg<DK, BC>;
     constexpr int NT = C::PREP_NT, PW = NT / 64;  // threads, waves
     constexpr int C8 = DK / 8;                    // 16-byte channel groups per row
@@ -308,6 +313,13 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
     const int pair = blk / nch, ci = blk % nch;
     const int b = pair / c.H, h = pair % c.H;
     const float lg = c.log2g[h];
+    if (xz) {
+        // the chunk kernel's GroupNorm exchange words of this block (BC xns,
+        // contiguous), and its ticket counters, start at zero
+        u32x4 *xr = reinterpret_cast<u32x4 *>(xz + (size_t)blk * BC * xns);
+        for (int i = tid; i < BC * xns / 2; i += NT) xr[i] = u32x4{0u, 0u, 0u, 0u};
+        if (blk == 0 && tid < 8) xtick[tid] = 0u;
+    }
     for (int t = tid; t < BC; t += NT) {
         dec[t] = c.scale * exp2f((float)t * lg);
         if (PAR)  // s gamma^(T-1-t) for absolute token t
@@ -642,9 +654,12 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     // real values overwrite later (stores of one wave to one address stay in
     // order), so that every chunk issues the same stores.
     // row offsets are 32-bit within the batch row: T H d_v < 2^31
-    uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 4 * g;
+    // lane (l16, g) stores columns 32 p + 8 g .. + 7 of its row for each
+    // pair p of column tiles (see the packing below)
+    uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 8 * g;
     float2 *sbase_st = a.stats ? a.stats + (size_t)b * c.T * c.H * a.NS + slice : nullptr;
-    uint32_t pend_o[C::NQT][C::CT][2];
+    static_assert(C::CT % 2 == 0, "column tiles come in pairs");
+    uint32_t pend_o[C::NQT][C::CT / 2][4];
     uint32_t pend_row[C::NQT];  // t H + h within the batch row
     float2 pend_stat[C::NQT];
 #pragma unroll
@@ -652,7 +667,7 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         pend_row[u] = (uint32_t)(i0 * BC + 16 * qt[u] + l16) * c.H + h;
         pend_stat[u] = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
+        for (int p = 0; p < C::CT / 2; ++p) pend_o[u][p][0] = pend_o[u][p][1] = pend_o[u][p][2] = pend_o[u][p][3] = 0u;
     }
     const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
     const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
@@ -660,9 +675,9 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     auto flush_u = [&](int u) {
         uint16_t *dst = obase + pend_row[u] * (uint32_t)c.dv;
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
-            const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
-            *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+        for (int p = 0; p < C::CT / 2; ++p) {
+            const u32x4 v4 = {pend_o[u][p][0], pend_o[u][p][1], pend_o[u][p][2], pend_o[u][p][3]};
+            *reinterpret_cast<u32x4 *>(dst + p * 32) = v4;
         }
         if (stats_out && g == 0) sbase_st[pend_row[u] * (uint32_t)a.NS] = pend_stat[u];
     };
@@ -852,11 +867,25 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                         for (int r = 0; r < 4; ++r) oacc[u][ct][r] = (oacc[u][ct][r] - mean) * inv;
                 }
             }
+            // Lane (l16, g) holds columns 16 ct + 4 g .. + 3 of row l16.
+            // For each pair of column tiles, exchanging the upper half of
+            // the first with the lower half of the second
+            // (permlane32_swap), then the odd 16-lane rows of the first
+            // result with the even rows of the second (permlane16_swap),
+            // leaves columns 8 g .. 8 g + 7 of the pair in lane group g,
+            // so each row of the pair leaves as one 64-byte piece.
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                pend_o[u][ct][0] = pack_bf16x2(oacc[u][ct][0], oacc[u][ct][1]);
-                pend_o[u][ct][1] = pack_bf16x2(oacc[u][ct][2], oacc[u][ct][3]);
-            }
+            for (int p = 0; p < C::CT / 2; ++p)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const auto s32 =
+                        __builtin_amdgcn_permlane32_swap(pack_bf16x2(oacc[u][2 * p][2 * i], oacc[u][2 * p][2 * i + 1]),
+                                                         pack_bf16x2(oacc[u][2 * p + 1][2 * i], oacc[u][2 * p + 1][2 * i + 1]),
+                                                         false, false);
+                    const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                    pend_o[u][p][i] = s16[0];
+                    pend_o[u][p][2 + i] = s16[1];
+                }
         }
         write_st(Sn);
     };
@@ -921,12 +950,39 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 //     chunk), so no direct-to-LDS load is outstanding when the compiler
 //     waits for a fragment;
 //   - P^T fragments of key blocks a query tile does not reach are not loaded.
-template <int DK, int BC>
+//
+// GroupNorm exchange (XG, 2 <= NS <= 8 slices per row).  The NS workgroups
+// of a (pair, segment) run through the same chunks side by side, so instead
+// of leaving slice partials to gn_finalize_kernel (a second pass over O),
+// each O wave publishes the (mean, M2) of its rows' 64 columns at the end of
+// a chunk, as one 8-byte word per row and slice written with a device-scope
+// atomic store: the mean's bits, then M2's with the sign bit set, which marks
+// the word as written (prep_kernel zeroes the words first; M2 >= 0).  A word
+// is single-copy atomic, so no fence is needed.  The wave keeps the bf16
+// outputs of chunk cj in an LDS ring, loads the NS words of their rows with
+// device-scope atomic loads at the start of chunk cj + 2 (a whole chunk ahead
+// of use, and a chunk after the slices wrote them), and at the end of chunk
+// cj + 2, once every word is marked (reloading until then), combines them --
+// mean of the slice means, M2 = sum of the slice M2 + 64 (mean_s - mean)^2 --
+// and stores the normalised rows.  The words of a (pair, chunk) are laid out
+// per 16-row tile as [slice][row], so that a slice's words of a tile are one
+// cache line: the loads add few requests to a kernel bound by them.
+// The wait cannot deadlock: workgroups take tickets from a counter in the
+// order they start and the slices of a (pair, segment) hold consecutive
+// tickets, so when any of them waits, all of the earliest waiting group have
+// started, and that group never waits on a later one.  The wait is bounded
+// (a budget of reloads per wave); rows whose words it never saw marked would
+// be stored as NaN.
+template <int DK, int BC, bool XG>
 __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
     static_assert(C::NW == 4 && C::QSTAGE, "warp-specialised pass: 4 + 4 waves, Q~ fragments carry xi");
     __shared__ __attribute__((aligned(16))) char Vb0[C::VTILE], Vb1[C::VTILE];
     __shared__ __attribute__((aligned(16))) __bf16 St0[W * C::SP], St1[W * C::SP];  // S_old^T
+    // exchange: each O wave's bf16 outputs of the last two chunks
+    constexpr int RING = 2 * C::NW * C::NQT * (C::CT / 2) * 1024;
+    static_assert(!XG || 2 * C::VTILE + 4 * W * C::SP + RING <= 163840, "LDS budget (exchange ring)");
+    __shared__ __attribute__((aligned(16))) char Ob[XG ? RING : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool srole = w8 >= C::NW;
@@ -935,7 +991,20 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
     const int npairs = c.B * c.H;
     int pair, seg, slice;
     {
-        const int id = blockIdx.x, nps = npairs * a.nseg;
+        const int nps = npairs * a.nseg;
+        int id = blockIdx.x;
+        if constexpr (XG) {
+            // tickets in start order, one queue per XCD-sized group of ids
+            // when the (pair, segment) groups stay within one (see above)
+            __shared__ int ticket;
+            if (tid == 0) {
+                const int qu = nps % 8 == 0 ? (int)(blockIdx.x & 7) : 0;
+                const int t = (int)__hip_atomic_fetch_add(a.xtick + qu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ticket = nps % 8 == 0 ? 8 * t + qu : t;
+            }
+            __syncthreads();
+            id = ticket;
+        }
         int ps;
         if (nps % 8 == 0) {
             const int xcd = id & 7, j = id >> 3;
@@ -1112,9 +1181,12 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                 if (32 * kb <= 16 * qt[u] + 15)
                     pr[u][kb % C::R] = ldfrag(pfb, (size_t)(ci * C::NKT + qt[u]) * C::NB + kb);
         };
-        uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 4 * g;
+        // lane (l16, g) stores columns 32 p + 8 g .. + 7 of its row for each
+        // pair p of column tiles (see the packing below)
+        uint16_t *obase = a.o + (size_t)b * c.T * c.H * c.dv + col0 + 8 * g;
         float2 *sbase_st = a.stats ? a.stats + (size_t)b * c.T * c.H * a.NS + slice : nullptr;
-        uint32_t pend_o[C::NQT][C::CT][2];
+        static_assert(C::CT % 2 == 0, "column tiles come in pairs");
+        uint32_t pend_o[C::NQT][C::CT / 2][4];
         uint32_t pend_row[C::NQT];
         float2 pend_stat[C::NQT];
 #pragma unroll
@@ -1122,19 +1194,93 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
             pend_row[u] = (uint32_t)(i0 * BC + 16 * qt[u] + l16) * c.H + h;
             pend_stat[u] = make_float2(0.f, 0.f);
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) pend_o[u][ct][0] = pend_o[u][ct][1] = 0u;
+            for (int p = 0; p < C::CT / 2; ++p) pend_o[u][p][0] = pend_o[u][p][1] = pend_o[u][p][2] = pend_o[u][p][3] = 0u;
         }
-        const bool stats_out = a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
-        const bool norm_here = a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+        const bool stats_out = !XG && a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
+        const bool norm_here = !XG && a.NS == 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM);
         const int64_t rp0 = (c.flags & MSR_FLAG_DECAY_ROWNORM) ? row_pos0(c, b) : 0;
         auto flush_u = [&](int u) {
             uint16_t *dst = obase + pend_row[u] * (uint32_t)c.dv;
 #pragma unroll
-            for (int ct = 0; ct < C::CT; ++ct) {
-                const u32x2 v2 = {pend_o[u][ct][0], pend_o[u][ct][1]};
-                *reinterpret_cast<u32x2 *>(dst + ct * 16) = v2;
+            for (int p = 0; p < C::CT / 2; ++p) {
+                const u32x4 v4 = {pend_o[u][p][0], pend_o[u][p][1], pend_o[u][p][2], pend_o[u][p][3]};
+                *reinterpret_cast<u32x4 *>(dst + p * 32) = v4;
             }
-            if (stats_out && g == 0) sbase_st[pend_row[u] * (uint32_t)a.NS] = pend_stat[u];
+            if constexpr (!XG)
+                if (stats_out && g == 0) sbase_st[pend_row[u] * (uint32_t)a.NS] = pend_stat[u];
+        };
+        // GroupNorm exchange: lane group g takes the words of slices g and
+        // g + 4 of its row.  The bf16 outputs of chunk cj wait in LDS slot
+        // cj & 1 until the end of chunk cj + 2; the words of chunk cj are
+        // loaded at the start of chunk cj + 2, a whole chunk ahead of use.
+        // Words of a (pair, chunk) are contiguous, per 16-row tile [slice][row]:
+        // a slice's 16 words of a tile fill one 128-byte line, and a tile's
+        // words for all slices NS lines.
+        unsigned long long *const xw =
+            XG ? reinterpret_cast<unsigned long long *>(a.stats) + (size_t)pair * nch * BC * a.NS : nullptr;
+        unsigned long long xs[XG ? C::NQT : 1][2];
+        auto xrow = [&](int cj, int u) { return (uint32_t)(cj * BC + 16 * qt[u] + l16) * c.H + h; };
+        // word of (chunk cj, tile u, slice sl) for this lane's row
+        auto xword = [&](int cj, int u, int sl) {
+            return xw + ((size_t)cj * BC + 16 * qt[u]) * a.NS + sl * 16 + l16;
+        };
+        const float rns = 1.f / (float)a.NS, rdv = 1.f / (float)c.dv;
+        auto xload = [&](int cj, int u) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (g + 4 * j < a.NS)
+                    xs[u][j] = __hip_atomic_load(xword(cj, u, g + 4 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto xmarked = [&](int u) {
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (g + 4 * j < a.NS) ok = ok && (xs[u][j] >> 63) != 0ull;
+            return ok;
+        };
+        auto ring = [&](int cj, int u, int p) {
+            return reinterpret_cast<u32x4 *>(Ob + ((((cj & 1) * C::NW + w) * C::NQT + u) * (C::CT / 2) + p) * 1024 +
+                                             lane * 16);
+        };
+        // combine chunk cj's words, normalise its held-back outputs and store
+        // them; the reloads a wave may spend waiting are bounded over the
+        // whole kernel
+        int xbudget = 1 << 16;
+        auto xfinish = [&](int cj, int u) {
+            if (!__all(xmarked(u))) {
+                do {
+                    --xbudget;
+                    __builtin_amdgcn_s_sleep(2);
+                    xload(cj, u);
+                } while (!__all(xmarked(u)) && xbudget > 0);
+            }
+            float sm = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (g + 4 * j < a.NS) sm += __uint_as_float((uint32_t)xs[u][j]);
+            const float mean = sum_lane_groups(sm) * rns;
+            float m2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (g + 4 * j < a.NS) {
+                    const float d = __uint_as_float((uint32_t)xs[u][j]) - mean;
+                    m2 += __uint_as_float((uint32_t)(xs[u][j] >> 32) & 0x7fffffffu) + (float)W * d * d;
+                }
+            m2 = sum_lane_groups(m2);
+            // (x - mean) / sqrt(var + eps) as one fma per value
+            float inv = __builtin_amdgcn_rsqf(m2 * rdv + c.eps);
+            if (!__all(xmarked(u))) inv = __builtin_nanf("");
+            const float sh = -mean * inv;
+            uint16_t *dst = obase + xrow(cj, u) * (uint32_t)c.dv;
+#pragma unroll
+            for (int p = 0; p < C::CT / 2; ++p) {
+                u32x4 x = *ring(cj, u, p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = pack_bf16x2(__builtin_fmaf(__uint_as_float(x[e] << 16), inv, sh),
+                                       __builtin_fmaf(__uint_as_float(x[e] & 0xffff0000u), inv, sh));
+                *reinterpret_cast<u32x4 *>(dst + p * 32) = x;
+            }
         };
         if (i1 > i0) {
             load_q(i0, 0, C::NQ);
@@ -1145,6 +1291,11 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         auto chunk = [&](int ci, const char *Vc, const __bf16 *Sc) {
             const int t0 = ci * BC;
             __syncthreads();
+            if constexpr (XG)
+                if (ci - 2 >= i0) {
+#pragma unroll
+                    for (int u = 0; u < C::NQT; ++u) xload(ci - 2, u);
+                }
             s16x4 va[2][C::CT][2];  // V^T of blocks kb (even/odd)
             auto read_va = [&](int kb, s16x4 (&d)[C::CT][2]) {
 #pragma unroll
@@ -1176,11 +1327,13 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                             oacc[u][ct] = mfma16(fr[ks % (FD + 1)][ct], qr[u][ks],
                                                  ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[u][ct]);
                     vmem_fence();
-                    if (ks < C::NQT) flush_u(ks);
+                    if (!XG && ks < C::NQT) flush_u(ks);
                     vmem_fence();
                 }
+                if constexpr (!XG) {
 #pragma unroll
-                for (int i = C::KS; i < C::NQT; ++i) flush_u(i);
+                    for (int i = C::KS; i < C::NQT; ++i) flush_u(i);
+                }
                 vmem_fence();
             }
 #pragma unroll
@@ -1202,6 +1355,8 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
             }
 #pragma unroll
             for (int u = 0; u < C::NQT; ++u) {
+                if constexpr (XG)
+                    if (ci - 2 >= i0) xfinish(ci - 2, u);
                 const int jq = 16 * qt[u] + l16;
                 pend_row[u] = (uint32_t)(t0 + jq) * c.H + h;
                 if (c.flags & MSR_FLAG_DECAY_ROWNORM) {
@@ -1209,7 +1364,23 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
 #pragma unroll
                     for (int ct = 0; ct < C::CT; ++ct) oacc[u][ct] = oacc[u][ct] * f;
                 }
-                if (norm_here || stats_out) {
+                if constexpr (XG) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct) sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
+                    const float mean = sum_lane_groups(sum) * (1.f / W);
+                    float m2 = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) m2 += (oacc[u][ct][r] - mean) * (oacc[u][ct][r] - mean);
+                    m2 = sum_lane_groups(m2);
+                    if (g == 0)
+                        __hip_atomic_store(xword(ci, u, slice),
+                                           (unsigned long long)__float_as_uint(mean) |
+                                               ((unsigned long long)(__float_as_uint(m2) | 0x80000000u) << 32),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else if (norm_here || stats_out) {
                     float sum = 0.f;
 #pragma unroll
                     for (int ct = 0; ct < C::CT; ++ct) sum += oacc[u][ct][0] + oacc[u][ct][1] + oacc[u][ct][2] + oacc[u][ct][3];
@@ -1229,10 +1400,24 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                             for (int r = 0; r < 4; ++r) oacc[u][ct][r] = (oacc[u][ct][r] - mean) * inv;
                     }
                 }
+                // the same lane swaps as in chunk_mfma_kernel: columns
+                // 8 g .. + 7 of each pair of column tiles end in lane group g
 #pragma unroll
-                for (int ct = 0; ct < C::CT; ++ct) {
-                    pend_o[u][ct][0] = pack_bf16x2(oacc[u][ct][0], oacc[u][ct][1]);
-                    pend_o[u][ct][1] = pack_bf16x2(oacc[u][ct][2], oacc[u][ct][3]);
+                for (int p = 0; p < C::CT / 2; ++p)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const auto s32 =
+                            __builtin_amdgcn_permlane32_swap(pack_bf16x2(oacc[u][2 * p][2 * i], oacc[u][2 * p][2 * i + 1]),
+                                                             pack_bf16x2(oacc[u][2 * p + 1][2 * i], oacc[u][2 * p + 1][2 * i + 1]),
+                                                             false, false);
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                        pend_o[u][p][i] = s16[0];
+                        pend_o[u][p][2 + i] = s16[1];
+                    }
+                if constexpr (XG) {
+#pragma unroll
+                    for (int p = 0; p < C::CT / 2; ++p)
+                        *ring(ci, u, p) = u32x4{pend_o[u][p][0], pend_o[u][p][1], pend_o[u][p][2], pend_o[u][p][3]};
                 }
             }
         };
@@ -1241,8 +1426,17 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
             if (ci + 1 < i1) chunk(ci + 1, Vb1, St1);
         }
         if (i1 > i0) {
+            if constexpr (XG) {
+                for (int cj = i1 - 2 >= i0 ? i1 - 2 : i0; cj < i1; ++cj) {
 #pragma unroll
-            for (int u = 0; u < C::NQT; ++u) flush_u(u);
+                    for (int u = 0; u < C::NQT; ++u) xload(cj, u);
+#pragma unroll
+                    for (int u = 0; u < C::NQT; ++u) xfinish(cj, u);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < C::NQT; ++u) flush_u(u);
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -1619,14 +1813,16 @@ void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const voi
         hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
-                           static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo));
+                           static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo),
+                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick);
     } else {
         constexpr auto pk = prep_kernel<DK, BC, false, false, QPERM>;
         const unsigned grid = C::PREP_PERSIST ? fill_grid<pk>(C::PREP_NT, nblk) : (unsigned)nblk;
         hipLaunchKernelGGL(pk, dim3(grid), dim3(C::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
-                           (const uint16_t *)nullptr, (const uint16_t *)nullptr);
+                           (const uint16_t *)nullptr, (const uint16_t *)nullptr,
+                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick);
     }
 }
 
@@ -1657,8 +1853,13 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, bool wide, const 
     }
     main_kernel_begin(st);
     if constexpr (C::NW == 4 && C::QSTAGE) {
-        auto ck = chunk_ws_kernel<DK, BC>;
-        hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
+        if (a.xtick) {
+            auto ck = chunk_ws_kernel<DK, BC, true>;
+            hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
+        } else {
+            auto ck = chunk_ws_kernel<DK, BC, false>;
+            hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
+        }
     } else {
         auto ck = chunk_mfma_kernel<DK, BC, false>;
         hipLaunchKernelGGL(ck, dim3(grid), dim3(C::THREADS), 0, st, c, a);
@@ -1680,11 +1881,12 @@ hipError_t dispatch_bc(const MsrConst &c, const ChunkArgs &a, bool wide, int chu
 }
 
 struct MfmaPlan {
-    size_t qf = 0, kf = 0, pf = 0, stats = 0, segE = 0, total = 0;
+    size_t qf = 0, kf = 0, pf = 0, stats = 0, segE = 0, tick = 0, total = 0;
     int nseg = 1;
     int NS = 1;          // GroupNorm partials per row
     bool wide = false;   // 256-column slices (k_chunk_wide.hip)
     bool fused = false;  // the fused kernel (k_chunk_fused.hip): no fragments
+    bool xg = false;     // GroupNorm exchange between the slices of a row (chunk_ws_kernel)
 };
 
 // Segments per pair: doubled while the workgroups (pairs x value slices x
@@ -1728,9 +1930,13 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk, bool split = false) {
     const bool wide_ok = chunk_wide_supported(p->dk, p->dv, chunk) && !(p->flags & kFlagNoWide);
     m.wide = wide_ok && (chunk == 64 || choose_nseg(p, chunk, 256) == 1);
     m.NS = p->dv / (m.wide ? 32 : W);  // GroupNorm partials per row
+    // the warp-specialised kernel (b <= 128) normalises the rows itself when
+    // they span 2 to 8 of its slices, exchanging slice statistics
+    m.xg = !m.wide && chunk <= 128 && m.NS >= 2 && m.NS <= 8 && !(p->flags & MSR_FLAG_NO_GROUPNORM);
     m.segE = m.stats + (m.NS > 1 ? up(tokens * m.NS * sizeof(float2)) : 0);
     m.nseg = choose_nseg(p, chunk, m.wide ? 256 : W);
-    m.total = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
+    m.tick = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
+    m.total = m.tick + (m.xg ? 256 : 0);
     return m;
 }
 
@@ -1767,7 +1973,7 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     const unsigned pgrid = Cfg<DK, 64>::PREP_PERSIST ? fill_grid<pk>(Cfg<DK, 64>::PREP_NT, pblk) : (unsigned)pblk;
     hipLaunchKernelGGL(pk, dim3(pgrid), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq, (const uint16_t *)nullptr,
-                       (const uint16_t *)nullptr);
+                       (const uint16_t *)nullptr, (unsigned long long *)nullptr, 0, (unsigned *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
@@ -1885,6 +2091,7 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.nseg = m.nseg;
     a.seglen = p->T / chunk / m.nseg;
     a.segE = m.nseg > 1 ? reinterpret_cast<float *>(wsb + m.segE) : nullptr;
+    a.xtick = m.xg ? reinterpret_cast<unsigned *>(wsb + m.tick) : nullptr;
 
     hipError_t e = hipSuccess;
     switch (p->dk) {
@@ -1894,7 +2101,7 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     default: e = hipErrorNotSupported;
     }
     if (e != hipSuccess) return e;
-    if (a.NS > 1 && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+    if (a.NS > 1 && !m.xg && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;
         const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
         hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, a.NS,

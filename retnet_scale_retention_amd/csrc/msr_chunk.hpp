@@ -25,12 +25,18 @@ struct ChunkArgs {
     uint16_t *o;
     const float *s_in;
     float *s_out;
-    float2 *stats;  // [B*T*H][NS] (mean, M2) of each 64-column slice, when NS > 1
+    float2 *stats;  // [B*T*H][NS] (mean, M2) of each 64-column slice, when NS > 1 (or the exchange words)
     int NS;         // 64-column slices per pair (dv / 64)
     int NW2;        // workgroup slices per pair of the wide kernel (dv / 256), else NS
     int nseg, seglen;  // segments of seglen chunks per pair (nseg * seglen = T / b)
     float *segE;       // [pair][nseg][dk][dv] end state of each segment from a zero state
     int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
+    // GroupNorm exchange between the value slices of a row (chunk_ws_kernel,
+    // 2 <= NS <= 8): eight ticket counters, null when the slices leave
+    // (mean, M2) partials to gn_finalize_kernel instead.  The slices' words
+    // live in `stats` (8 bytes each, [pair][chunk][tile][slice][16 rows]);
+    // prep_kernel zeroes both.
+    unsigned *xtick;
 };
 
 // Argument block of the fused chunk kernel (k_chunk_fused.hip), which reads

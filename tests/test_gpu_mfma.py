@@ -304,3 +304,38 @@ def test_mfma_segmented_state_out_aliases_state_in(case):
     eo, es = out_err(down(o), ro), state_err(down(sd), rs)
     note(f"  O err {eo:.2e}  state err {es:.2e}")
     assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
+# Rows spanning 2 to 8 of the 64-column kernel's slices at b <= 128: the
+# slices exchange GroupNorm statistics inside the chunk kernel.  Cases cover
+# an odd slice count, pair counts that are and are not multiples of 8 (the
+# workgroups' ticket queues), segments, and b = 64 / 128.  Besides the
+# slice-normwise bound, every row must be close on its own, so that one
+# mis-normalised row or chunk cannot hide in a slice's norm.
+XG_CASES = [  # (B, T, H, dk, dv, chunk)
+    (1, 256, 3, 64, 512, 128),
+    (2, 512, 4, 64, 320, 64),
+    (1, 1024, 2, 256, 448, 128),
+    (1, 384, 1, 64, 512, 64),
+    (2, 1024, 4, 128, 192, 128),
+]
+
+
+@pytest.mark.parametrize("case", XG_CASES, ids=lambda c: "B%dT%dH%ddk%ddv%db%d" % c)
+def test_mfma_slice_exchange_vs_oracle(case):
+    B, T, H, dk, dv, b = case
+    w = mi.Workload("mfma-xg", 86, B, T, H, dk, dv, "bf16", (b,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = mi.gammas(H)
+    note(f"slice exchange {case}: oracle")
+    ro, rs = orc.recurrent(q, k, v, g, s_in=s, pos0=7)
+    note(f"slice exchange {case}: gpu")
+    o1, st = run(q, k, v, g, b, s_in=s, pos0=7)
+    o2, _ = run(q, k, v, g, b, s_in=s, pos0=7)
+    eo, es = out_err(o1, ro), state_err(st, rs)
+    rows = np.linalg.norm((o1 - ro).reshape(-1, dv), axis=1) / np.maximum(np.linalg.norm(ro.reshape(-1, dv), axis=1), 1e-30)
+    note(f"  O err {eo:.2e}  state err {es:.2e}  worst row {rows.max():.2e}")
+    assert np.array_equal(o1, o2)
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+    assert np.isfinite(o1).all() and rows.max() < 0.25
