@@ -1444,10 +1444,13 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
 
 // Parallel form (jsqmd.com s4.1; aiqz.cc "parallel representation"):
 //   O[n] = GN( sum_{m<=n} s gamma^(n-m) (q~_n . k~_m) v_m + gamma^(n+1) q~_n S_in )
-// One workgroup of four waves per (pair, block of 64 queries, value slice
-// of PW columns: 256 when d_v allows, else 64); wave w owns query tile
-// 4 qb + w.  The scores are formed once per slice, so the wider slice does
-// them a quarter as often.  Per 32-key block up to the
+// One workgroup of NWV waves per (pair, block of queries, value slice of PW
+// columns: 256 when d_v allows, else 64); each wave owns NQW query tiles of
+// 16, so a block holds 64, 128 or (eight waves) 256 queries.  The scores are
+// formed once per slice, so the wider slice does them a quarter as often,
+// and every wave of the workgroup shares the loads of a key block: the kernel
+// is bound by the loads each CU keeps in flight, so more queries per load
+// means more matrix work per request.  Per 32-key block up to the
 // diagonal, the K~ fragments (prep_kernel, PAR) and the V slice stream into
 // double-buffered LDS by direct loads; each wave forms P^T = K~ Q~^T with
 // bf16 MFMA, applies s gamma^(n-m) and the causal mask in registers, and
@@ -1464,16 +1467,19 @@ struct ParArgs {
     int NS;
 };
 
-template <int DK, int PW, int NQW>
-__global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs a) {
+template <int DK, int PW, int NQW, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void parallel_mfma_kernel(MsrConst c, ParArgs a) {
     using C = Cfg<DK, 64>;
     constexpr int KS = DK / 32;
     constexpr int CT = PW / 16;            // 16-column tiles of the slice
-    constexpr int QB = 64 * NQW;           // queries per workgroup
+    constexpr int NT = NWV * NQW;          // query tiles per workgroup
+    constexpr int QB = 16 * NT;            // queries per workgroup
     constexpr int KBYTES = 2 * KS * 1024;  // K~ fragments of one 32-key block
     constexpr int VBYTES = 32 * PW * 2;    // V slice of one 32-key block
-    constexpr int NVL = VBYTES / 1024 / 4; // 1 KiB direct loads of it per wave
-    static_assert(PW % 64 == 0 && NVL >= 1 && (NQW == 1 || NQW == 2), "slice width, query tiles per wave");
+    constexpr int NVL = VBYTES / 1024 / NWV;  // 1 KiB direct loads of it per wave
+    static_assert(PW % 64 == 0 && NVL >= 1 && NVL * NWV * 1024 == VBYTES && (NQW == 1 || NQW == 2) &&
+                      (NWV == 4 || NWV == 8),
+                  "slice width, query tiles per wave, waves");
     // V rows (PW 2 bytes) with their 16-byte chunks XOR-swizzled by row so
     // that the transpose reads of a 16-lane group (4 rows x 32 bytes) spread
     // over the banks
@@ -1511,12 +1517,12 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     const int b = pair / c.H, h = pair % c.H;
     const int col0 = slice * PW;
     const float lg = c.log2g[h];
-    // this wave's query tiles: 4 qb + w, or with two per wave 8 qb + w and
-    // 8 qb + 7 - w (equal causal work across the waves)
+    // this wave's query tiles: NT qb + w, and with two per wave also
+    // NT qb + NT - 1 - w (equal causal work across the waves)
     int tile[NQW], n[NQW];
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
-        tile[i] = i == 0 ? 4 * NQW * qb + w : 8 * qb + 7 - w;
+        tile[i] = i == 0 ? NT * qb + w : NT * qb + NT - 1 - w;
         n[i] = 16 * tile[i] + l16;  // this lane's query row (as MFMA column)
     }
     const uint32_t loff = lane * 16;
@@ -1530,10 +1536,10 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
     // consecutive fragments of the Q~-layout array; V rows 32 kb ..
     auto dma = [&](int kb, char *kd, char *vd) {
         const char *ks = reinterpret_cast<const char *>(kqb + (size_t)(2 * kb) * KS * FRAG);
-        for (int u = w; u < 2 * KS; u += 4) load_lds16(ks + u * 1024 + loff, kd + u * 1024);
+        for (int u = w; u < 2 * KS; u += NWV) load_lds16(ks + u * 1024 + loff, kd + u * 1024);
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
-            const int unit = 4 * i + w, byte = unit * 1024 + lane * 16;
+            const int unit = NWV * i + w, byte = unit * 1024 + lane * 16;
             const int row = byte / (PW * 2), phys = (byte % (PW * 2)) >> 4;
             load_lds16(vb + (uint32_t)(32 * kb + row) * rowV + (phys ^ vswz(row)) * 16, vd + unit * 1024);
         }
@@ -1557,7 +1563,7 @@ __global__ __launch_bounds__(256) void parallel_mfma_kernel(MsrConst c, ParArgs 
         for (int sc = 0; sc < PW / W; ++sc) {
             const float *sp = a.s_in + (size_t)pair * DK * c.dv + col0 + sc * W;
             if (sc > 0) __syncthreads();  // every wave is done with the previous columns
-            for (int e = tid; e < DK * W; e += 256) {
+            for (int e = tid; e < DK * W; e += 64 * NWV) {
                 const int row = e / W, col = e % W;
                 St[col * C::SP + row] = static_cast<__bf16>(sp[(size_t)row * c.dv + col]);
             }
@@ -1979,11 +1985,18 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
     main_kernel_begin(st);
     // two query tiles per wave (128 queries per workgroup) when T allows: each
-    // K~ and V fragment read from LDS then serves two MFMAs
+    // K~ and V fragment read from LDS then serves two MFMAs; with 256-column
+    // slices and T a multiple of 256, eight waves (256 queries) share each
+    // block's K~ and V loads
     const int nq2 = c.T % 128 == 0 ? 2 : 1;
-    auto ok = PW == 256 ? (nq2 == 2 ? parallel_mfma_kernel<DK, 256, 2> : parallel_mfma_kernel<DK, 256, 1>)
-                        : (nq2 == 2 ? parallel_mfma_kernel<DK, 64, 2> : parallel_mfma_kernel<DK, 64, 1>);
-    hipLaunchKernelGGL(ok, dim3(npairs * (c.T / (64 * nq2)) * NSO), dim3(256), 0, st, c, pa);
+    if (PW == 256 && c.T % 256 == 0) {
+        hipLaunchKernelGGL((parallel_mfma_kernel<DK, 256, 2, 8>), dim3(npairs * (c.T / 256) * NSO), dim3(512), 0, st,
+                           c, pa);
+    } else {
+        auto ok = PW == 256 ? (nq2 == 2 ? parallel_mfma_kernel<DK, 256, 2> : parallel_mfma_kernel<DK, 256, 1>)
+                            : (nq2 == 2 ? parallel_mfma_kernel<DK, 64, 2> : parallel_mfma_kernel<DK, 64, 1>);
+        hipLaunchKernelGGL(ok, dim3(npairs * (c.T / (64 * nq2)) * NSO), dim3(256), 0, st, c, pa);
+    }
     e = hipGetLastError();
     main_kernel_end(st);
     if (e != hipSuccess) return e;

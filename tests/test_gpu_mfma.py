@@ -146,6 +146,10 @@ PAR_CASES = [  # (B, T, H, dk, dv); d_v a multiple of 256 takes 256-column outpu
     (2, 128, 2, 64, 256),
     (1, 320, 2, 128, 256),
     (1, 192, 2, 256, 512),
+    # 256-column slices with T a multiple of 256: eight-wave workgroups of 256 queries
+    (1, 512, 2, 128, 256),
+    (2, 768, 1, 256, 512),
+    (1, 256, 3, 64, 256),
 ]
 
 
