@@ -1617,13 +1617,15 @@ __global__ __launch_bounds__(64 * NWV) void parallel_mfma_kernel(MsrConst c, Par
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kb + 1 < nkb) dma(kb + 1, Kn, Vn);
-        bool act[NQW];  // the tile reaches this block (uniform)
+        // Skip the block when none of the wave's tiles reaches it.  A tile
+        // that does not (the first of two, near the diagonal) is still
+        // computed: its scores all fall under the causal mask, so it adds
+        // zero, and the products stay one straight run of MFMAs -- guarding
+        // each product by the tile turns every MFMA into a basic block of its
+        // own, which the scheduler cannot overlap with the LDS reads.
         bool any = false;
 #pragma unroll
-        for (int i = 0; i < NQW; ++i) {
-            act[i] = 32 * kb <= 16 * tile[i] + 15;
-            any = any || act[i];
-        }
+        for (int i = 0; i < NQW; ++i) any = any || 32 * kb <= 16 * tile[i] + 15;
         if (!any) return;
         f32x4 acc[NQW][2];
 #pragma unroll
@@ -1634,13 +1636,11 @@ __global__ __launch_bounds__(64 * NWV) void parallel_mfma_kernel(MsrConst c, Par
             for (int v2 = 0; v2 < 2; ++v2) {
                 const bf16x8 A = *reinterpret_cast<const bf16x8 *>(Kc + (v2 * KS + ks) * 1024 + loff);
 #pragma unroll
-                for (int i = 0; i < NQW; ++i)
-                    if (act[i]) acc[i][v2] = mfma16(A, qr[i][ks], acc[i][v2]);
+                for (int i = 0; i < NQW; ++i) acc[i][v2] = mfma16(A, qr[i][ks], acc[i][v2]);
             }
         bf16x8 pb[NQW];
 #pragma unroll
         for (int i = 0; i < NQW; ++i) {
-            if (!act[i]) continue;
             const float base = c.scale * exp2f((float)(n[i] - 32 * kb - 31) * lg) * dg;
             float f[8];
 #pragma unroll
@@ -1667,8 +1667,7 @@ __global__ __launch_bounds__(64 * NWV) void parallel_mfma_kernel(MsrConst c, Par
             const s16x4 v1 = lds_tr(va + 16 * PW * 2);
             const bf16x8 Vf = cat(v0, v1);
 #pragma unroll
-            for (int i = 0; i < NQW; ++i)
-                if (act[i]) oacc[i][ct] = mfma16(Vf, pb[i], oacc[i][ct]);
+            for (int i = 0; i < NQW; ++i) oacc[i][ct] = mfma16(Vf, pb[i], oacc[i][ct]);
         }
     };
     for (int kb = 0; kb < nkb; kb += 2) {
