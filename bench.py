@@ -6,7 +6,8 @@ products, decay mask, cross-chunk term, state carry, GroupNorm) over the
 7B-shaped layer: B=2, T=8192, H=16, d_k=256, d_v=512, chunk 128, bf16 in,
 fp32 state.  `value` is that forward's throughput in tokens/s with inputs
 already resident in HBM.  The same JSON line also reports
-  - roofline: the chunk-recurrence kernel alone (the dominant kernel), timed
+  - roofline: the chunk-recurrence kernel alone (the dominant kernel, which
+    also normalises the rows when they span 2-8 of its slices), timed
     with HIP events recorded around it on its own stream (library measurement
     hook), against the bf16 dense MFMA peak, with its algorithmic flops
     4 d_k d_v (inter-chunk term and state update) + (b+1) d_v (causal value
@@ -210,24 +211,25 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     for _ in range(warmup):
         msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
     ev = HipEvents(steps)
-    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # the timed steps: back-to-back calls, with the library recording the
+    # main kernel's events (the roofline's kernel time) and nothing else
     t0.record()
     for i in range(steps):
         msr.set_kernel_events(*ev.pairs[i])
-        calls[i][0].record()
         msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws)
-        calls[i][1].record()
     msr.set_kernel_events(None, None)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     kern_ms = [ev.elapsed_ms(i) for i in range(steps)]
-    call_ms = [a.elapsed_time(b) for a, b in calls]
     ev.close()
     ms = total_ms / steps
+    # per-call durations (median, min) from events around each call, after the timed steps
+    call_ms = per_call_ms(torch, lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s, workspace=ws),
+                          steps)
     # the same call with a 512 MiB cache flush before each rep
     flushed = stats_ms(per_call_ms(torch, lambda: msr.msr_chunkwise(qd, kd, vd, g, chunk, out=o, state_out=s,
                                                                     workspace=ws), steps, Flusher(torch)))
@@ -592,8 +594,10 @@ def cpu_baseline(mi, chunk):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the warm-up is long enough (about 40 ms of calls) for the GPU to reach its
+    # steady clocks: the first tens of calls after a pause run up to 10% slower
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")

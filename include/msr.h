@@ -289,12 +289,16 @@ msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k
 
 /*
  * Measurement hook (optional).  When `start` and `stop` are non-NULL
- * hipEvent_t handles, each later compute call made on this host thread
- * records `start` on its stream immediately before its main kernel and
- * `stop` immediately after it: the chunk-recurrence kernel of msr_chunkwise,
- * the output kernel of msr_parallel, the kernel of msr_recurrent_step.  The
- * caller owns the events; NULL, NULL switches the hook off.  The hook only
- * records events: results are unchanged.
+ * hipEvent_t handles (created with timing), each later compute call made on
+ * this host thread records them at the start and the end of its main kernel:
+ * the chunk-recurrence kernel of msr_chunkwise, the output kernel of
+ * msr_parallel, the kernel of msr_recurrent_step.  For the matrix-core
+ * chunk and parallel kernels and the decode kernels the events are attached
+ * to the kernel's own dispatch (hipExtLaunchKernel), so the hook adds no
+ * commands to the stream; elsewhere they are recorded on the call's stream
+ * right before and after the kernel.  The caller owns the events; NULL, NULL
+ * switches the hook off.  The hook only records events: results are
+ * unchanged.
  */
 void msr_set_kernel_events(void *start, void *stop);
 

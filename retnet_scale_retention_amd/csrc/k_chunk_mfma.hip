@@ -1856,22 +1856,15 @@ hipError_t launch_chunk(const MsrConst &c, const ChunkArgs &a, bool wide, const 
         hipLaunchKernelGGL(sk, dim3(grid), dim3(C::THREADS), 0, st, c, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    main_kernel_begin(st);
     if constexpr (C::NW == 4 && C::QSTAGE) {
-        if (a.xtick) {
-            auto ck = chunk_ws_kernel<DK, BC, true>;
-            hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
-        } else {
-            auto ck = chunk_ws_kernel<DK, BC, false>;
-            hipLaunchKernelGGL(ck, dim3(grid), dim3(2 * C::THREADS), 0, st, c, a);
-        }
+        if (a.xtick)
+            launch_main(chunk_ws_kernel<DK, BC, true>, dim3(grid), dim3(2 * C::THREADS), st, c, a);
+        else
+            launch_main(chunk_ws_kernel<DK, BC, false>, dim3(grid), dim3(2 * C::THREADS), st, c, a);
     } else {
-        auto ck = chunk_mfma_kernel<DK, BC, false>;
-        hipLaunchKernelGGL(ck, dim3(grid), dim3(C::THREADS), 0, st, c, a);
+        launch_main(chunk_mfma_kernel<DK, BC, false>, dim3(grid), dim3(C::THREADS), st, c, a);
     }
-    e = hipGetLastError();
-    main_kernel_end(st);
-    return e;
+    return hipGetLastError();
 }
 
 template <int DK>
@@ -1982,22 +1975,19 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
-    main_kernel_begin(st);
     // two query tiles per wave (128 queries per workgroup) when T allows: each
     // K~ and V fragment read from LDS then serves two MFMAs; with 256-column
     // slices and T a multiple of 256, eight waves (256 queries) share each
     // block's K~ and V loads
     const int nq2 = c.T % 128 == 0 ? 2 : 1;
     if (PW == 256 && c.T % 256 == 0) {
-        hipLaunchKernelGGL((parallel_mfma_kernel<DK, 256, 2, 8>), dim3(npairs * (c.T / 256) * NSO), dim3(512), 0, st,
-                           c, pa);
+        launch_main(parallel_mfma_kernel<DK, 256, 2, 8>, dim3(npairs * (c.T / 256) * NSO), dim3(512), st, c, pa);
     } else {
         auto ok = PW == 256 ? (nq2 == 2 ? parallel_mfma_kernel<DK, 256, 2> : parallel_mfma_kernel<DK, 256, 1>)
                             : (nq2 == 2 ? parallel_mfma_kernel<DK, 64, 2> : parallel_mfma_kernel<DK, 64, 1>);
-        hipLaunchKernelGGL(ok, dim3(npairs * (c.T / (64 * nq2)) * NSO), dim3(256), 0, st, c, pa);
+        launch_main(ok, dim3(npairs * (c.T / (64 * nq2)) * NSO), dim3(256), st, c, pa);
     }
     e = hipGetLastError();
-    main_kernel_end(st);
     if (e != hipSuccess) return e;
     // outgoing state after the outputs, which read s_in (s_out may alias it)
     if (s_out) {

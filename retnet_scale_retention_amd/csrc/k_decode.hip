@@ -310,9 +310,8 @@ template <typename TIn, int NT>
 void launch_nt(const MsrConst &c, const void *q, const void *k, const void *v, void *o, const float *s_in,
                float *s_out, hipStream_t st) {
     auto kern = decode_kernel<TIn, NT>;
-    hipLaunchKernelGGL(kern, dim3(c.B * c.H), dim3(DEC_THREADS), 0, st, c, static_cast<const TIn *>(q),
-                       static_cast<const TIn *>(k), static_cast<const TIn *>(v), static_cast<TIn *>(o), s_in,
-                       s_out);
+    launch_main(kern, dim3(c.B * c.H), dim3(DEC_THREADS), st, c, static_cast<const TIn *>(q),
+                static_cast<const TIn *>(k), static_cast<const TIn *>(v), static_cast<TIn *>(o), s_in, s_out);
 }
 
 template <typename TIn>
@@ -335,13 +334,13 @@ hipError_t launch_decode(const MsrConst &c, int dtype, const void *q, const void
     if (c.T == 1 && s_in && s_in == s_out) {  // one step in place
         const int pairs = c.B * c.H;
         if (dtype == MSR_BF16)
-            hipLaunchKernelGGL(decode_step_kernel<uint16_t>, dim3(pairs), dim3(DEC_THREADS), 0, st, c,
-                               static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                               static_cast<const uint16_t *>(v), static_cast<uint16_t *>(o), s_out);
+            launch_main(decode_step_kernel<uint16_t>, dim3(pairs), dim3(DEC_THREADS), st, c,
+                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                        static_cast<const uint16_t *>(v), static_cast<uint16_t *>(o), s_out);
         else
-            hipLaunchKernelGGL(decode_step_kernel<float>, dim3(pairs), dim3(DEC_THREADS), 0, st, c,
-                               static_cast<const float *>(q), static_cast<const float *>(k),
-                               static_cast<const float *>(v), static_cast<float *>(o), s_out);
+            launch_main(decode_step_kernel<float>, dim3(pairs), dim3(DEC_THREADS), st, c,
+                        static_cast<const float *>(q), static_cast<const float *>(k),
+                        static_cast<const float *>(v), static_cast<float *>(o), s_out);
         return hipGetLastError();
     }
     if (dtype == MSR_BF16)

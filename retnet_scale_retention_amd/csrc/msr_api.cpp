@@ -514,6 +514,9 @@ void main_kernel_end(hipStream_t st) {
     if (g_ev_stop) (void)hipEventRecord(g_ev_stop, st);
 }
 
+hipEvent_t main_event_start() { return g_ev_start; }
+hipEvent_t main_event_stop() { return g_ev_stop; }
+
 extern "C" {
 
 int msr_abi_version(void) { return MSR_ABI_VERSION; }
@@ -593,9 +596,7 @@ msr_status msr_parallel(const msr_problem *p, const void *Q, const void *K, cons
     if (mfma_supported(p, MSR_FORM_PARALLEL, p->T))
         return hip_status(mfma_parallel(c, p, Q, K, V, O, state_in, state_out, ws, st), "mfma parallel");
     if (p->T <= MSR_DECODE_MAX_T) {  // a few tokens: the recurrence, one pass over the state
-        main_kernel_begin(st);
         const hipError_t e = launch_decode(c, p->dtype, Q, K, V, O, state_in, state_out, st);
-        main_kernel_end(st);
         return hip_status(e, "short parallel");
     }
 
@@ -638,9 +639,7 @@ msr_status msr_chunkwise(const msr_problem *p, int32_t chunk, const void *Q, con
         return hip_status(mfma_chunkwise(c, p, chunk, Q, K, V, O, state_in, state_out, ws, st),
                           "mfma chunkwise");
     if (p->T <= MSR_DECODE_MAX_T) {  // a few tokens: one pass over the state (the result is independent of b)
-        main_kernel_begin(st);
         const hipError_t e = launch_decode(c, p->dtype, Q, K, V, O, state_in, state_out, st);
-        main_kernel_end(st);
         return hip_status(e, "short chunkwise");
     }
 
@@ -826,9 +825,8 @@ msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k
         return fail(MSR_ERR_INVALID_ARG, "o must not alias q, k, v or state");
     const MsrConst c = make_const(p, 1);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    main_kernel_begin(st);
+    // (launch_decode attaches the kernel events to the step kernel itself)
     const hipError_t e = launch_decode(c, p->dtype, q, k, v, o, state, state, st);
-    main_kernel_end(st);
     return hip_status(e, "decode step");
 }
 

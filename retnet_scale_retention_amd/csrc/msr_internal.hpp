@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "msr.h"
@@ -97,3 +98,16 @@ hipError_t static_scratch(void **ptr);
 // around the main kernel of a call on its stream.  No-ops when unset.
 void main_kernel_begin(hipStream_t st);
 void main_kernel_end(hipStream_t st);
+// The caller's events (null when unset), and a launch of a call's main
+// kernel that attaches them to the kernel's own dispatch (its start and end
+// times) rather than recording them as separate commands around it.
+hipEvent_t main_event_start();
+hipEvent_t main_event_stop();
+template <typename F, typename... Args>
+inline void launch_main(F kern, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    const hipEvent_t a = main_event_start(), b = main_event_stop();
+    if (a && b)
+        hipExtLaunchKernelGGL(kern, grid, block, 0u, st, a, b, 0u, args...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+}
