@@ -625,16 +625,32 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                 for (int r = 0; r < 4; ++r) {
                     const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
                     float x = 0.f;
-                    if (!SO) {
+                    if (!SO)
                         x = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
-                        for (int gg = 0; gg < seg; ++gg)
-                            x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
-                        x *= f0;
-                    } else if (a.par && a.s_in) {  // gamma^T s_in
+                    else if (a.par && a.s_in)  // gamma^T s_in
                         x = a.s_in[sbase + (size_t)row * c.dv + col] * exp2f((float)c.T * lg);
-                    }
                     S[rt][ct][r] = x;
                 }
+        if (!SO) {
+            // earlier segments' end states, one whole tile set per segment
+            // (the loads of a segment are independent, so they overlap)
+            for (int gg = 0; gg < seg; ++gg) {
+                const float *e = a.segE + ebase + (size_t)gg * DK * c.dv;
+#pragma unroll
+                for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                            S[rt][ct][r] = S[rt][ct][r] * gseg + e[(size_t)row * c.dv + col];
+                        }
+            }
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * f0;
+        }
     }
     auto write_st = [&](__bf16 *St) {
 #pragma unroll
@@ -1079,11 +1095,25 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                        float x = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
-                        for (int gg = 0; gg < seg; ++gg)
-                            x = x * gseg + a.segE[ebase + ((size_t)gg * DK + row) * c.dv + col];
-                        S[rt][ct][r] = x * f0;
+                        S[rt][ct][r] = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
                     }
+            // earlier segments' end states, one whole tile set per segment
+            for (int gg = 0; gg < seg; ++gg) {
+                const float *e = a.segE + ebase + (size_t)gg * DK * c.dv;
+#pragma unroll
+                for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < C::CPW; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
+                            S[rt][ct][r] = S[rt][ct][r] * gseg + e[(size_t)row * c.dv + col];
+                        }
+            }
+#pragma unroll
+            for (int rt = 0; rt < C::RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < C::CPW; ++ct) S[rt][ct] = S[rt][ct] * f0;
         }
         auto write_st = [&](__bf16 *St) {
 #pragma unroll
