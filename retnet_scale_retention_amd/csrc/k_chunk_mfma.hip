@@ -986,9 +986,10 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 // The wait cannot deadlock: workgroups take tickets from a counter in the
 // order they start and the slices of a (pair, segment) hold consecutive
 // tickets, so when any of them waits, all of the earliest waiting group have
-// started, and that group never waits on a later one.  The wait is bounded
-// (a budget of reloads per wave); rows whose words it never saw marked would
-// be stored as NaN.
+// started, and that group never waits on a later one.  The slices run side by
+// side only when the whole grid is resident at once, which the launch
+// requires before it picks this mode.  The wait is bounded (10 s per wave);
+// rows whose words it never saw marked would be stored as NaN.
 template <int DK, int BC, bool XG>
 __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
@@ -1273,16 +1274,17 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                                              lane * 16);
         };
         // combine chunk cj's words, normalise its held-back outputs and store
-        // them; the reloads a wave may spend waiting are bounded over the
-        // whole kernel
-        int xbudget = 1 << 16;
+        // them; the time a wave may spend waiting over the whole kernel is
+        // bounded (10 s on the 100 MHz real-time counter)
+        uint64_t xwaited = 0;
         auto xfinish = [&](int cj, int u) {
-            if (!__all(xmarked(u))) {
+            if (!__all(xmarked(u)) && xwaited < 1000000000ull) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                 do {
-                    --xbudget;
                     __builtin_amdgcn_s_sleep(2);
                     xload(cj, u);
-                } while (!__all(xmarked(u)) && xbudget > 0);
+                } while (!__all(xmarked(u)) && xwaited + (__builtin_amdgcn_s_memrealtime() - t0) < 1000000000ull);
+                xwaited += __builtin_amdgcn_s_memrealtime() - t0;
             }
             float sm = 0.f;
 #pragma unroll
@@ -1837,6 +1839,28 @@ unsigned fill_grid(int threads, size_t nblk) {
     return (unsigned)(nblk < (size_t)n ? nblk : (size_t)n);
 }
 
+// Workgroups of the exchanging chunk_ws_kernel<dk, b> the current device
+// holds at once (0 where that kernel does not exist).
+template <int DK, int BC>
+unsigned xg_resident_bc() {
+    using C = Cfg<DK, BC>;
+    if constexpr (C::NW == 4 && C::QSTAGE)
+        return fill_grid<chunk_ws_kernel<DK, BC, true>>(2 * C::THREADS, (size_t)1 << 30);
+    else
+        return 0;
+}
+unsigned xg_resident(int dk, int bc) {
+    switch (dk * 1000 + bc) {
+    case 64064: return xg_resident_bc<64, 64>();
+    case 64128: return xg_resident_bc<64, 128>();
+    case 128064: return xg_resident_bc<128, 64>();
+    case 128128: return xg_resident_bc<128, 128>();
+    case 256064: return xg_resident_bc<256, 64>();
+    case 256128: return xg_resident_bc<256, 128>();
+    default: return 0;
+    }
+}
+
 template <int DK, int BC, bool QPERM>
 void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const void *K, const void *Qlo,
                  const void *Klo, hipStream_t st) {
@@ -1914,7 +1938,7 @@ struct MfmaPlan {
     int NS = 1;          // GroupNorm partials per row
     bool wide = false;   // 256-column slices (k_chunk_wide.hip)
     bool fused = false;  // the fused kernel (k_chunk_fused.hip): no fragments
-    bool xg = false;     // GroupNorm exchange between the slices of a row (chunk_ws_kernel)
+    bool xg = false;     // the GroupNorm exchange may be used (chunk_ws_kernel; space for its counters)
 };
 
 // Segments per pair: doubled while the workgroups (pairs x value slices x
@@ -2123,7 +2147,10 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.nseg = m.nseg;
     a.seglen = p->T / chunk / m.nseg;
     a.segE = m.nseg > 1 ? reinterpret_cast<float *>(wsb + m.segE) : nullptr;
-    a.xtick = m.xg ? reinterpret_cast<unsigned *>(wsb + m.tick) : nullptr;
+    // the exchange needs every slice of a (pair, segment) running at once:
+    // the whole grid resident together (else the separate GroupNorm pass)
+    const bool xg = m.xg && (size_t)p->B * p->H * m.nseg * m.NS <= xg_resident(p->dk, chunk);
+    a.xtick = xg ? reinterpret_cast<unsigned *>(wsb + m.tick) : nullptr;
 
     hipError_t e = hipSuccess;
     switch (p->dk) {
@@ -2133,7 +2160,7 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     default: e = hipErrorNotSupported;
     }
     if (e != hipSuccess) return e;
-    if (a.NS > 1 && !m.xg && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
+    if (a.NS > 1 && !xg && !(c.flags & MSR_FLAG_NO_GROUPNORM)) {
         const size_t rows = (size_t)p->B * p->T * p->H;
         const size_t blocks = (rows * (p->dv / 32) + 255) / 256;
         hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, a.NS,

@@ -311,7 +311,8 @@ def test_mfma_segmented_state_out_aliases_state_in(case):
 
 
 # Rows spanning 2 to 8 of the 64-column kernel's slices at b <= 128: the
-# slices exchange GroupNorm statistics inside the chunk kernel.  Cases cover
+# slices exchange GroupNorm statistics inside the chunk kernel when its whole
+# grid is resident at once.  Cases cover
 # an odd slice count, pair counts that are and are not multiples of 8 (the
 # workgroups' ticket queues), segments, and b = 64 / 128.  Besides the
 # slice-normwise bound, every row must be close on its own, so that one
@@ -322,6 +323,9 @@ XG_CASES = [  # (B, T, H, dk, dv, chunk)
     (1, 1024, 2, 256, 448, 128),
     (1, 384, 1, 64, 512, 64),
     (2, 1024, 4, 128, 192, 128),
+    # 64 pairs x 8 slices: more workgroups than the GPU holds at once, so the
+    # rows take the separate GroupNorm pass instead of the exchange
+    (4, 256, 16, 64, 512, 128),
 ]
 
 
