@@ -65,9 +65,9 @@
 extern "C" {
 #endif
 
-/* 5: MSR_FLAG_FUSED (4: msr_workspace_bytes, msr_chunkwise_noalloc; strong-decay routing; 3: MSR_FLAG_DECAY_ROWNORM,
+/* 6: msr_set_exchange; 5: MSR_FLAG_FUSED (4: msr_workspace_bytes, msr_chunkwise_noalloc; strong-decay routing; 3: MSR_FLAG_DECAY_ROWNORM,
  * msr_qkv_projection, msr_qkv_chunkwise; 2: pos_rows) */
-#define MSR_ABI_VERSION 5
+#define MSR_ABI_VERSION 6
 #define MSR_MAX_HEADS 128 /* H limit (per-head constants travel by value) */
 #define MSR_MAX_DK 512    /* d_k limit (theta values travel by value) */
 #define MSR_MAX_DV 1024   /* d_v limit */
@@ -301,6 +301,32 @@ msr_status msr_recurrent_step(const msr_problem *p, const void *q, const void *k
  * unchanged.
  */
 void msr_set_kernel_events(void *start, void *stop);
+
+/*
+ * How msr_chunkwise's matrix-core chunk kernel finishes GroupNorm when a row's
+ * d_v columns are split over several workgroups (GroupNorm over the heads'
+ * outputs: jsqmd.com section 3, aiqz.cc "gated multi-scale retention").
+ * Process-wide; applies to every later call on any device.
+ *   MSR_EXCHANGE_AUTO (the default): when the call's whole grid can be resident
+ *     at once, the workgroups of a row exchange their partial statistics
+ *     through device memory and each normalises its own columns, waiting for
+ *     its peers (at most 10 s, then it proceeds with what it has).  Of calls
+ *     that overlap on one device only one waits at a time (a device-wide
+ *     claim that the waiting call hands back once all its workgroups have
+ *     started); the others take the MSR_EXCHANGE_NO_WAIT route.
+ *   MSR_EXCHANGE_OFF: never wait; a separate GroupNorm pass follows the chunk
+ *     kernel (about 2 us slower on the 7B-sized layer).  For callers that keep
+ *     kernels of their own spinning on the device alongside, which the
+ *     exchange's waits could otherwise outlast.
+ *   MSR_EXCHANGE_NO_WAIT: the route a call takes when another call holds the
+ *     claim: it stores un-normalised rows, and the last of each (pair,
+ *     segment)'s workgroups to finish normalises that segment's rows from the
+ *     exchanged statistics (one workgroup per segment: slower).  Selectable
+ *     so that the route can be checked on its own.
+ * Returns MSR_ERR_INVALID_ARG (and changes nothing) for any other value.
+ */
+typedef enum { MSR_EXCHANGE_AUTO = 0, MSR_EXCHANGE_OFF = 1, MSR_EXCHANGE_NO_WAIT = 2 } msr_exchange_mode;
+msr_status msr_set_exchange(int32_t mode);
 
 #ifdef __cplusplus
 }

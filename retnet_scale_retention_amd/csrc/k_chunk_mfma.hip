@@ -52,9 +52,30 @@
 // use, so the loads have most of a chunk to land.  Every wave issues the same
 // loads in the same order each chunk, so one fixed vmcnt wait tells when the
 // next V slice has landed.
+#include <atomic>
+
 #include "msr_chunk.hpp"
 #include "msr_device.hpp"
 #include "msr_mfma.hpp"
+
+namespace msr {
+// The call (its nonzero id) whose chunk kernel may wait on slice statistics
+// and does not yet have all of its workgroups resident, or 0; one word per
+// device, zero when the library loads.  A call that finds another owner runs
+// without waiting (it stores raw rows, which the last workgroup of each
+// (pair, segment) normalises from the slices' words).  The owner hands the
+// word back once its last workgroup has started: from then on it completes
+// on its own, so two calls that overlap on one GPU can never wait on each
+// other's workgroups.
+__device__ unsigned g_xg_owner;
+
+// The exchange's counter words: 16, then one per (pair, segment); after
+// them, from a 256-byte boundary, NEUTRAL_WORDS slice words that a call
+// which does not wait reads in place of its row's words: mean 0 and an M2
+// that makes the row's scale 1, so that it stores its rows unnormalised.
+constexpr int NEUTRAL_WORDS = 128;
+__host__ __device__ inline int xg_counter_words(int groups) { return (16 + groups + 63) / 64 * 64; }
+}  // namespace msr
 
 namespace {
 
@@ -246,7 +267,8 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
                                                                   const uint16_t *__restrict__ qlo = nullptr,
                                                                   const uint16_t *__restrict__ klo = nullptr,
                                                                   unsigned long long *__restrict__ xz = nullptr,
-                                                                  int xns = 0, unsigned *__restrict__ xtick = nullptr) {
+                                                                  int xns = 0, unsigned *__restrict__ xtick = nullptr,
+                                                                  unsigned xid = 0, int xng = 0) {
     using C = Cfg<DK, BC>;
     constexpr int NT = C::PREP_NT, PW = NT / 64;  // threads, waves
     constexpr int C8 = DK / 8;                    // 16-byte channel groups per row
@@ -318,7 +340,35 @@ __global__ __launch_bounds__((Cfg<DK, BC>::PREP_NT)) void prep_kernel(MsrConst c
         // contiguous), and its ticket counters, start at zero
         u32x4 *xr = reinterpret_cast<u32x4 *>(xz + (size_t)blk * BC * xns);
         for (int i = tid; i < BC * xns / 2; i += NT) xr[i] = u32x4{0u, 0u, 0u, 0u};
-        if (blk == 0 && tid < 8) xtick[tid] = 0u;
+        // and decides whether the chunk kernel may wait on the slices' words:
+        // mode 1 if this call claims the device's exchange, 2 if another
+        // call holds it (a replay of this same call included) or the call
+        // has no id.  Words 0-7 are the ticket queues, which carry the mode
+        // in their top bit (one atomic gives a workgroup its ticket and the
+        // mode), word 8 the mode, word 9 the count of queues whose
+        // workgroups have all started (the chunk kernel hands the claim back
+        // at the last), words 16 .. 16 + xng - 1 the finished workgroups of
+        // each (pair, segment) in mode 2.
+        if (blk == 0) {
+            if (tid == 0) {
+                unsigned prev = 1u;  // (no id: as if claimed)
+                if (xid) {
+                    prev = 0u;
+                    __hip_atomic_compare_exchange_strong(&g_xg_owner, &prev, xid, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                }
+                const unsigned md = prev == 0u ? 1u : 2u;
+                for (int q = 0; q < 8; ++q) xtick[q] = md == 2u ? 0x80000000u : 0u;
+                xtick[8] = md;
+            }
+            for (int i = 9 + tid; i < 16 + xng; i += NT) xtick[i] = 0u;
+            // neutral words: each slice M2 = (1 - eps) d_v / NS, so the row's
+            // variance plus eps is 1
+            unsigned long long *xn = reinterpret_cast<unsigned long long *>(xtick + xg_counter_words(xng));
+            const float m2n = (1.f - c.eps) * (float)c.dv / (float)xns;
+            for (int i = tid; i < NEUTRAL_WORDS; i += NT)
+                xn[i] = (unsigned long long)(__float_as_uint(m2n) | 0x80000000u) << 32;
+        }
     }
     for (int t = tid; t < BC; t += NT) {
         dec[t] = c.scale * exp2f((float)t * lg);
@@ -950,6 +1000,52 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// What a chunk kernel that did not wait for the slices' words needs at its
+// end to normalise a (pair, segment)'s rows from them.
+struct XgEnd {
+    const unsigned long long *words;  // [pair][16-row tile][slice][16 rows], 8 bytes each
+    uint16_t *o;
+    unsigned *tick;  // the exchange's counters
+    float eps;
+    unsigned id;     // the call's id
+    int ps;          // pair nseg + segment
+    int NS, nseg, rows, T, H, dv;  // rows: of a segment
+};
+
+// The GroupNorm of pair's rows t0 .. t0 + e.rows - 1 from the slices' words
+// (the slice's mean, then its M2 with the sign bit set), by one workgroup
+// (threads tid of nt), a thread normalising 32 values of a row at a time.
+// The row's mean is the mean of the slice means, its M2 the sum of the slice
+// M2 plus W (slice mean - row mean)^2.
+__device__ __forceinline__ void normalise_from_words(const XgEnd &e, int tid, int nt) {
+    const int tpr = e.dv / 32;  // threads per row, 32 values each
+    const int pair = e.ps / e.nseg, t0 = e.ps % e.nseg * e.rows;
+    const int b = pair / e.H, h = pair % e.H;
+    for (int gid = tid; gid < e.rows * tpr; gid += nt) {
+        const int t = t0 + gid / tpr;
+        const unsigned long long *wr = e.words + ((size_t)pair * e.T + (t & ~15)) * e.NS + (t & 15);
+        float mean = 0.f;
+        for (int sl = 0; sl < e.NS; ++sl) mean += __uint_as_float((uint32_t)wr[16 * sl]);
+        mean /= (float)e.NS;
+        float m2 = 0.f;
+        for (int sl = 0; sl < e.NS; ++sl) {
+            const float d = __uint_as_float((uint32_t)wr[16 * sl]) - mean;
+            m2 += __uint_as_float((uint32_t)(wr[16 * sl] >> 32) & 0x7fffffffu) + (float)W * d * d;
+        }
+        const float inv = 1.f / sqrtf(m2 / (float)e.dv + e.eps);
+        u32x4 *p = reinterpret_cast<u32x4 *>(e.o + (((size_t)b * e.T + t) * e.H + h) * e.dv) + gid % tpr;
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 x = p[i * tpr];
+            u32x4 y;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                y[k] = pack_bf16x2((__uint_as_float(x[k] << 16) - mean) * inv,
+                                   (__uint_as_float(x[k] & 0xffff0000u) - mean) * inv);
+            p[i * tpr] = y;
+        }
+    }
+}
+
 // Warp-specialised variant of the full pass (b <= 128): 8 waves, two per
 // SIMD.  The four "O" waves (w < 4) run the inter-chunk product, the value
 // product and GroupNorm with the fragments of chunk kernel wave w; the four
@@ -988,8 +1084,16 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
 // tickets, so when any of them waits, all of the earliest waiting group have
 // started, and that group never waits on a later one.  The slices run side by
 // side only when the whole grid is resident at once, which the launch
-// requires before it picks this mode.  The wait is bounded (10 s per wave);
-// rows whose words it never saw marked would be stored as NaN.
+// requires before it picks this mode, and only one call at a time may wait
+// before its grid is all resident: its prep_kernel claims the device's
+// exchange (g_xg_owner), which its last workgroup to start hands back.  A
+// call that finds the exchange claimed by another runs the same code on
+// neutral words (mean 0, scale 1: it never waits and stores its rows
+// unnormalised), and the last of a (pair, segment)'s workgroups to finish
+// normalises that segment's rows from the real words (one workgroup per
+// segment, so slower; this only happens when calls overlap).  The wait is
+// bounded (10 s per wave); rows whose words it never saw marked would be
+// stored as NaN.
 template <int DK, int BC, bool XG>
 __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(MsrConst c, ChunkArgs a) {
     using C = Cfg<DK, BC>;
@@ -1007,20 +1111,43 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
     const int l16 = lane & 15, g = lane >> 4;
     const int npairs = c.B * c.H;
     int pair, seg, slice;
+    // exchange state that is read rarely, kept in LDS rather than in
+    // registers across the chunk loop: the call's mode (1: wait for the
+    // slices' words, 2: store rows raw) and what the kernel's end needs
+    __shared__ unsigned xs_mode;
+    __shared__ XgEnd xs_end;
+    bool xlastq = false;  // (thread 0) the owner's last workgroup to start in its ticket queue
+    unsigned xqc = 0u;    // (thread 0 of those) the queues counted, itself included (8: release the claim)
     {
         const int nps = npairs * a.nseg;
         int id = blockIdx.x;
         if constexpr (XG) {
             // tickets in start order, one queue per XCD-sized group of ids
-            // when the (pair, segment) groups stay within one (see above)
+            // when the (pair, segment) groups stay within one (see above),
+            // and the call's mode in the ticket's top bit: 1 = wait for the
+            // slices' words (this call owns the exchange), 2 = do not wait
+            // (another call owns it).  The owner's last workgroup to start
+            // hands the exchange back when it ends; with eight queues, the
+            // last to start in each queue counts its queue, and the one that
+            // counts the eighth hands it back (the count's reply is not
+            // waited for at the start).
             __shared__ int ticket;
             if (tid == 0) {
-                const int qu = nps % 8 == 0 ? (int)(blockIdx.x & 7) : 0;
-                const int t = (int)__hip_atomic_fetch_add(a.xtick + qu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ticket = nps % 8 == 0 ? 8 * t + qu : t;
+                const int nq = nps % 8 == 0 ? 8 : 1;
+                const int qu = nq == 8 ? (int)(blockIdx.x & 7) : 0;
+                const unsigned tk = __hip_atomic_fetch_add(a.xtick + qu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int t = (int)(tk & 0x7fffffffu);
+                const unsigned md = tk >> 31 ? 2u : 1u;
+                xlastq = md == 1u && t == (int)gridDim.x / nq - 1;
+                ticket = nq == 8 ? 8 * t + qu : t;
+                xs_mode = md;
             }
             __syncthreads();
             id = ticket;
+            if (xlastq)
+                xqc = nps % 8 == 0
+                          ? __hip_atomic_fetch_add(a.xtick + 9, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u
+                          : 8u;
         }
         int ps;
         if (nps % 8 == 0) {
@@ -1033,6 +1160,9 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         }
         pair = ps / a.nseg;
         seg = ps % a.nseg;
+        if (XG && tid == 0)
+            xs_end = XgEnd{reinterpret_cast<const unsigned long long *>(a.stats), a.o, a.xtick, c.eps, a.xid, ps,
+                           a.NS, a.nseg, a.seglen * BC, c.T, c.H, c.dv};
     }
     const int i0 = seg * a.seglen, i1 = i0 + a.seglen;
     const int b = pair / c.H, h = pair % c.H;
@@ -1247,20 +1377,30 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         // Words of a (pair, chunk) are contiguous, per 16-row tile [slice][row]:
         // a slice's 16 words of a tile fill one 128-byte line, and a tile's
         // words for all slices NS lines.
+        // A call that does not wait reads the neutral words instead (every
+        // offset masked into them) and never finds a word unmarked.
         unsigned long long *const xw =
             XG ? reinterpret_cast<unsigned long long *>(a.stats) + (size_t)pair * nch * BC * a.NS : nullptr;
+        const unsigned long long *xr = xw;
+        uint32_t xmask = 0xffffffffu;
+        if constexpr (XG) {
+            if (__builtin_amdgcn_readfirstlane(xs_mode) != 1u) {
+                xr = reinterpret_cast<const unsigned long long *>(a.xtick + xg_counter_words(npairs * a.nseg));
+                xmask = NEUTRAL_WORDS - 1;
+            }
+        }
         unsigned long long xs[XG ? C::NQT : 1][2];
         auto xrow = [&](int cj, int u) { return (uint32_t)(cj * BC + 16 * qt[u] + l16) * c.H + h; };
         // word of (chunk cj, tile u, slice sl) for this lane's row
-        auto xword = [&](int cj, int u, int sl) {
-            return xw + ((size_t)cj * BC + 16 * qt[u]) * a.NS + sl * 16 + l16;
-        };
+        auto xoff = [&](int cj, int u, int sl) { return (uint32_t)((cj * BC + 16 * qt[u]) * a.NS + sl * 16 + l16); };
+        auto xword = [&](int cj, int u, int sl) { return xw + xoff(cj, u, sl); };
         const float rns = 1.f / (float)a.NS, rdv = 1.f / (float)c.dv;
         auto xload = [&](int cj, int u) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 if (g + 4 * j < a.NS)
-                    xs[u][j] = __hip_atomic_load(xword(cj, u, g + 4 * j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    xs[u][j] = __hip_atomic_load(xr + (xoff(cj, u, g + 4 * j) & xmask), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
         };
         auto xmarked = [&](int u) {
             bool ok = true;
@@ -1472,6 +1612,30 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         }
     }
     __builtin_amdgcn_s_waitcnt(0);
+    if (XG && xqc == 8u) {
+        unsigned own = xs_end.id;
+        __hip_atomic_compare_exchange_strong(&g_xg_owner, &own, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (XG && xs_mode != 1u) {
+        // After a call that did not wait, the last of the NS workgroups of a
+        // (pair, segment) to finish normalises that segment's rows from the
+        // slices' words (the others' rows and words are released before
+        // their count, and acquired by it after the last count).
+        __shared__ int last;
+        __syncthreads();
+        const XgEnd e = xs_end;
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // (a device-wide L2 write-back)
+            last = __hip_atomic_fetch_add(e.tick + 16 + e.ps, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned)e.NS - 1;
+        }
+        __syncthreads();
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            normalise_from_words(e, tid, blockDim.x);
+        }
+    }
 }
 
 // Parallel form (jsqmd.com s4.1; aiqz.cc "parallel representation"):
@@ -1873,7 +2037,8 @@ void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const voi
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
                            static_cast<const uint16_t *>(Qlo), static_cast<const uint16_t *>(Klo),
-                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick);
+                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick, a.xid,
+                           c.B * c.H * a.nseg);
     } else {
         constexpr auto pk = prep_kernel<DK, BC, false, false, QPERM>;
         const unsigned grid = C::PREP_PERSIST ? fill_grid<pk>(C::PREP_NT, nblk) : (unsigned)nblk;
@@ -1881,7 +2046,8 @@ void launch_prep(const MsrConst &c, const ChunkArgs &a, const void *Q, const voi
                            static_cast<const uint16_t *>(K), const_cast<uint16_t *>(a.qf),
                            const_cast<uint16_t *>(a.kf), const_cast<uint16_t *>(a.pf), (uint16_t *)nullptr,
                            (const uint16_t *)nullptr, (const uint16_t *)nullptr,
-                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick);
+                           a.xtick ? reinterpret_cast<unsigned long long *>(a.stats) : nullptr, a.NS, a.xtick, a.xid,
+                           c.B * c.H * a.nseg);
     }
 }
 
@@ -1988,7 +2154,9 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk, bool split = false) {
     m.segE = m.stats + (m.NS > 1 ? up(tokens * m.NS * sizeof(float2)) : 0);
     m.nseg = choose_nseg(p, chunk, m.wide ? 256 : W);
     m.tick = m.segE + (m.nseg > 1 ? up((size_t)p->B * p->H * m.nseg * p->dk * p->dv * sizeof(float)) : 0);
-    m.total = m.tick + (m.xg ? 256 : 0);
+    m.total = m.tick + (m.xg ? xg_counter_words(p->B * p->H * m.nseg) * sizeof(unsigned) +
+                                   NEUTRAL_WORDS * sizeof(unsigned long long)
+                             : 0);
     return m;
 }
 
@@ -2025,7 +2193,7 @@ hipError_t launch_parallel(const MsrConst &c, const msr_problem *p, const void *
     const unsigned pgrid = Cfg<DK, 64>::PREP_PERSIST ? fill_grid<pk>(Cfg<DK, 64>::PREP_NT, pblk) : (unsigned)pblk;
     hipLaunchKernelGGL(pk, dim3(pgrid), dim3(Cfg<DK, 64>::PREP_NT), 0, st, c, static_cast<const uint16_t *>(Q),
                        static_cast<const uint16_t *>(K), qf, kf, (uint16_t *)nullptr, kq, (const uint16_t *)nullptr,
-                       (const uint16_t *)nullptr, (unsigned long long *)nullptr, 0, (unsigned *)nullptr);
+                       (const uint16_t *)nullptr, (unsigned long long *)nullptr, 0, (unsigned *)nullptr, 0u, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ParArgs pa{qf, kq, static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), s_in, stats, NSO};
@@ -2149,8 +2317,16 @@ hipError_t mfma_chunkwise(const MsrConst &c, const msr_problem *p, int chunk, co
     a.segE = m.nseg > 1 ? reinterpret_cast<float *>(wsb + m.segE) : nullptr;
     // the exchange needs every slice of a (pair, segment) running at once:
     // the whole grid resident together (else the separate GroupNorm pass)
-    const bool xg = m.xg && (size_t)p->B * p->H * m.nseg * m.NS <= xg_resident(p->dk, chunk);
+    const int xmode = exchange_mode();
+    const bool xg = m.xg && xmode != MSR_EXCHANGE_OFF &&
+                    (size_t)p->B * p->H * m.nseg * m.NS <= xg_resident(p->dk, chunk);
     a.xtick = xg ? reinterpret_cast<unsigned *>(wsb + m.tick) : nullptr;
+    if (xg && xmode == MSR_EXCHANGE_AUTO) {  // a nonzero id per call claims the exchange (0: never waits)
+        static std::atomic<unsigned> calls{0};
+        unsigned id = ++calls;
+        while (id == 0) id = ++calls;
+        a.xid = id;
+    }
 
     hipError_t e = hipSuccess;
     switch (p->dk) {

@@ -2,6 +2,7 @@
 // argument validation, per-call constants, workspace carving and dispatch
 // to the HIP kernels.  Validation completes before the first launch, so a
 // non-OK status never leaves partial results behind.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+std::atomic<int> g_exchange{MSR_EXCHANGE_AUTO};
 
 msr_status fail(msr_status s, const char *fmt, ...) {
     va_list ap;
@@ -514,6 +516,8 @@ void main_kernel_end(hipStream_t st) {
     if (g_ev_stop) (void)hipEventRecord(g_ev_stop, st);
 }
 
+int exchange_mode() { return g_exchange.load(std::memory_order_relaxed); }
+
 hipEvent_t main_event_start() { return g_ev_start; }
 hipEvent_t main_event_stop() { return g_ev_stop; }
 
@@ -524,6 +528,13 @@ int msr_abi_version(void) { return MSR_ABI_VERSION; }
 void msr_set_kernel_events(void *start, void *stop) {
     g_ev_start = static_cast<hipEvent_t>(start);
     g_ev_stop = static_cast<hipEvent_t>(stop);
+}
+
+msr_status msr_set_exchange(int32_t mode) {
+    if (mode != MSR_EXCHANGE_AUTO && mode != MSR_EXCHANGE_OFF && mode != MSR_EXCHANGE_NO_WAIT)
+        return fail(MSR_ERR_INVALID_ARG, "exchange mode %d is not one of 0, 1, 2", (int)mode);
+    g_exchange.store(mode, std::memory_order_relaxed);
+    return MSR_OK;
 }
 
 const char *msr_last_error(void) { return g_err; }

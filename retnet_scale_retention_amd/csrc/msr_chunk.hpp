@@ -32,11 +32,14 @@ struct ChunkArgs {
     float *segE;       // [pair][nseg][dk][dv] end state of each segment from a zero state
     int par;           // state-only pass of the parallel form: s_out = gamma^T s_in + sum of KF^T V
     // GroupNorm exchange between the value slices of a row (chunk_ws_kernel,
-    // 2 <= NS <= 8): eight ticket counters, null when the slices leave
+    // 2 <= NS <= 8): 16 + B H nseg counter words (eight ticket queues, the
+    // call's mode, queues all started, and per (pair, segment) the finished
+    // workgroups of a call that does not wait), null when the slices leave
     // (mean, M2) partials to gn_finalize_kernel instead.  The slices' words
     // live in `stats` (8 bytes each, [pair][chunk][tile][slice][16 rows]);
     // prep_kernel zeroes both.
     unsigned *xtick;
+    unsigned xid;  // the call's nonzero id (ownership of the exchange)
 };
 
 // Argument block of the fused chunk kernel (k_chunk_fused.hip), which reads

@@ -94,6 +94,9 @@ hipError_t launch_state_op(const MsrConst &c, int d1, int d2, const float *in, f
 constexpr size_t MSR_STATIC_SCRATCH_BYTES = MSR_NOALLOC_SCRATCH_BYTES;
 hipError_t static_scratch(void **ptr);
 
+// The process-wide msr_exchange_mode (msr_set_exchange).
+int exchange_mode();
+
 // Measurement hook (msr_set_kernel_events): records the caller's events
 // around the main kernel of a call on its stream.  No-ops when unset.
 void main_kernel_begin(hipStream_t st);

@@ -19,13 +19,14 @@ LIB_PATH = Path(os.environ.get("MSR_LIB", Path(__file__).resolve().parent / "lib
 MSR_OK = 0
 MSR_F32, MSR_BF16 = 0, 1
 MSR_FLAG_NO_ROTATE, MSR_FLAG_NO_GROUPNORM, MSR_FLAG_DECAY_ROWNORM, MSR_FLAG_SPLIT_SCORES, MSR_FLAG_FUSED = 1, 2, 4, 8, 16
+MSR_EXCHANGE_AUTO, MSR_EXCHANGE_OFF, MSR_EXCHANGE_NO_WAIT = 0, 1, 2
 MSR_FORM_PARALLEL, MSR_FORM_CHUNKWISE, MSR_FORM_STEP, MSR_FORM_BACKWARD, MSR_FORM_QKV_CHUNKWISE = 0, 1, 2, 3, 4
 STATUS = {0: "MSR_OK", -1: "MSR_ERR_INVALID_ARG", -2: "MSR_ERR_SHAPE", -3: "MSR_ERR_DTYPE",
           -4: "MSR_ERR_UNSUPPORTED", -5: "MSR_ERR_WORKSPACE", -6: "MSR_ERR_HIP"}
 
 EXPORTS = ("msr_abi_version", "msr_last_error", "msr_workspace_size", "msr_workspace_bytes", "msr_parallel",
            "msr_chunkwise", "msr_chunkwise_noalloc", "msr_chunkwise_backward", "msr_qkv_projection", "msr_qkv_chunkwise",
-           "msr_recurrent_step", "msr_set_kernel_events")
+           "msr_recurrent_step", "msr_set_kernel_events", "msr_set_exchange")
 
 
 class MsrError(RuntimeError):
@@ -83,6 +84,7 @@ def load():
     lib.msr_recurrent_step.restype = ctypes.c_int
     lib.msr_set_kernel_events.argtypes = [vp, vp]
     lib.msr_set_kernel_events.restype = None
+    lib.msr_set_exchange.argtypes, lib.msr_set_exchange.restype = [ctypes.c_int32], ctypes.c_int
     del fp
     _lib = lib
     return lib
@@ -349,3 +351,9 @@ def set_kernel_events(start=None, stop=None):
     or None) around the main kernel of every later call on this thread."""
     load().msr_set_kernel_events(ctypes.c_void_p(start) if start else None,
                                  ctypes.c_void_p(stop) if stop else None)
+
+
+def set_exchange(mode: int):
+    """Process-wide GroupNorm finishing of the split-row chunk kernel
+    (MSR_EXCHANGE_AUTO, MSR_EXCHANGE_OFF or MSR_EXCHANGE_NO_WAIT; include/msr.h)."""
+    _check(load().msr_set_exchange(int(mode)))

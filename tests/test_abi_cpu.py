@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(m.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.msr_abi_version() == 5
+    assert lib.msr_abi_version() == 6
 
 
 def test_problem_struct_layout_matches_the_header():
@@ -195,3 +195,14 @@ def test_null_problem_and_bytes():
     assert m.STATUS[lib.msr_workspace_size(None, 1, 16, ctypes.byref(n))] == "MSR_ERR_INVALID_ARG"
     assert m.STATUS[lib.msr_workspace_size(desc().ref, 1, 16, None)] == "MSR_ERR_INVALID_ARG"
     assert m.STATUS[lib.msr_workspace_size(desc().ref, 9, 16, ctypes.byref(n))] == "MSR_ERR_INVALID_ARG"
+
+
+def test_exchange_mode_accepts_its_three_values_only():
+    lib = msr.load()
+    for bad in (-1, 3, 1 << 20):
+        assert m.STATUS[lib.msr_set_exchange(bad)] == "MSR_ERR_INVALID_ARG"
+        assert "exchange mode" in lib.msr_last_error().decode()
+    for mode in (m.MSR_EXCHANGE_OFF, m.MSR_EXCHANGE_NO_WAIT, m.MSR_EXCHANGE_AUTO):
+        msr.set_exchange(mode)
+    with pytest.raises(m.MsrError):
+        msr.set_exchange(7)

@@ -347,3 +347,105 @@ def test_mfma_slice_exchange_vs_oracle(case):
     assert np.array_equal(o1, o2)
     assert eo < TOL["bf16"] and es < TOL["bf16"]
     assert np.isfinite(o1).all() and rows.max() < 0.25
+
+
+def tick_word(ws, B, T, H, dk, dv, b, k):
+    """Counter word k of the exchange (0-7: ticket queues, 8: the call's
+    mode, 9: queues whose workgroups have all started, 16 + pair nseg + seg:
+    finished workgroups of a call that does not wait), after the MFMA path's
+    Q~, K~^T and P^T fragments and slice words in the workspace; for calls
+    without segments whose regions are whole multiples of 256 bytes."""
+    import torch
+    tok = B * T * H
+    off = 2 * tok * dk * 2 + tok * b * 2 + tok * (dv // 64) * 8 + 4 * k
+    return int(ws[off:off + 4].cpu().view(torch.int32)[0])
+
+
+@pytest.mark.parametrize("mode", ["off", "no_wait"])
+@pytest.mark.parametrize("case", [XG_CASES[0], XG_CASES[1], XG_CASES[4]], ids=lambda c: "B%dT%dH%ddk%ddv%db%d" % c)
+def test_mfma_exchange_routes_vs_oracle(case, mode):
+    """The two routes that never wait on other workgroups -- a separate
+    GroupNorm pass (MSR_EXCHANGE_OFF) and raw rows normalised by the call's
+    last workgroup from the exchanged words (MSR_EXCHANGE_NO_WAIT, the route
+    of a call that overlaps another) -- against the oracle, and against the
+    waiting route to within one more bf16 rounding of the rows."""
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+    B, T, H, dk, dv, b = case
+    w = mi.Workload("mfma-xg", 86, B, T, H, dk, dv, "bf16", (b,))
+    q, k, v = mi.qkv(w)
+    s = mi.state(w, 0.05)
+    g = mi.gammas(H)
+    note(f"exchange route {mode} {case}: oracle")
+    ro, rs = orc.recurrent(q, k, v, g, s_in=s, pos0=7)
+    note(f"exchange route {mode} {case}: gpu")
+    o_wait, _ = run(q, k, v, g, b, s_in=s, pos0=7)
+    ws = torch.empty(msr.workspace_size(B, T, H, dk, dv, msr.MSR_BF16, g, msr.MSR_FORM_CHUNKWISE, b),
+                     dtype=torch.uint8, device=dev)
+    msr.set_exchange(msr.MSR_EXCHANGE_OFF if mode == "off" else msr.MSR_EXCHANGE_NO_WAIT)
+    try:
+        o1, st = run(q, k, v, g, b, s_in=s, pos0=7, workspace=ws)
+        o2, _ = run(q, k, v, g, b, s_in=s, pos0=7, workspace=ws)
+    finally:
+        msr.set_exchange(msr.MSR_EXCHANGE_AUTO)
+    eo, es, ew = out_err(o1, ro), state_err(st, rs), out_err(o1, o_wait)
+    note(f"  O err {eo:.2e}  state err {es:.2e}  vs waiting route {ew:.2e}")
+    if mode == "no_wait" and case == XG_CASES[0]:
+        words = [tick_word(ws, *case, i) for i in [8, 9] + list(range(16, 16 + B * H))]
+        note(f"  mode, queues started, finished per pair: {words}")
+        assert words[:2] == [2, 0] and words[2:] == [dv // 64] * (B * H)
+    assert np.array_equal(o1, o2)
+    assert eo < TOL["bf16"] and es < TOL["bf16"] and ew < 1e-2
+    assert np.isfinite(o1).all()
+
+
+def test_mfma_slice_exchange_concurrent_calls():
+    """Two exchanging calls that overlap on one GPU: call A fills 192 of the
+    GPU's workgroup slots for about a millisecond (24 pairs x 8 slices, no
+    segments); call B, on a second stream, starts meanwhile on the free CUs.
+    A call that finds the exchange claimed (its owner's workgroups not all
+    started yet) runs without waiting (mode 2), else it claims it and waits
+    (mode 1); both results must hold either way: B against the oracle, A
+    against the same call run alone (bitwise when it waited)."""
+    import time
+    torch, dev = torch_dev()
+    import retnet_scale_retention_amd as msr
+
+    ga = mi.gammas(24)
+    A = (1, 32768, 24, 64, 512, 128)
+    qa, ka = (mi.device_normal((1, 32768, 24, 64), sd, dev, torch.bfloat16) for sd in (71, 72))
+    va = mi.device_normal((1, 32768, 24, 512), 73, dev, torch.bfloat16)
+    wsa = torch.empty(msr.workspace_size(*A[:5], msr.MSR_BF16, ga, msr.MSR_FORM_CHUNKWISE, 128), dtype=torch.uint8,
+                      device=dev)
+    oa_alone = torch.empty_like(va)
+    msr.msr_chunkwise(qa, ka, va, ga, 128, out=oa_alone, workspace=wsa, return_state=False)
+    torch.cuda.synchronize()
+
+    Bc = (1, 256, 2, 64, 512, 128)
+    gb = mi.gammas(2)
+    w = mi.Workload("mfma-xg-conc", 87, *Bc[:5], "bf16", (128,))
+    q, k, v = mi.qkv(w)
+    note("concurrent exchange: oracle")
+    ro, _ = orc.recurrent(q, k, v, gb)
+    qb, kb, vb = (up(x, "bf16", dev) for x in (q, k, v))
+    wsb = torch.empty(msr.workspace_size(*Bc[:5], msr.MSR_BF16, gb, msr.MSR_FORM_CHUNKWISE, 128), dtype=torch.uint8,
+                      device=dev)
+    ob = torch.empty_like(vb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    note("concurrent exchange: A then B on two streams")
+    oa = torch.empty_like(va)
+    with torch.cuda.stream(sa):
+        msr.msr_chunkwise(qa, ka, va, ga, 128, out=oa, workspace=wsa, return_state=False)
+    time.sleep(3e-4)  # A's prologue (~0.1 ms) is over, its chunk kernel runs for ~1 ms
+    with torch.cuda.stream(sb):
+        msr.msr_chunkwise(qb, kb, vb, gb, 128, out=ob, workspace=wsb, return_state=False)
+    torch.cuda.synchronize()
+    ma, mb = tick_word(wsa, *A, 8), tick_word(wsb, *Bc, 8)
+    e = out_err(down(ob), ro)
+    note(f"  modes A {ma} B {mb}; B O err {e:.2e}")
+    assert ma in (1, 2) and mb in (1, 2)
+    if ma == 1:
+        assert torch.equal(oa, oa_alone)
+    else:
+        assert out_err(down(oa), down(oa_alone)) < 1e-2
+    assert np.isfinite(down(ob)).all() and e < TOL["bf16"]
