@@ -1061,7 +1061,9 @@ __device__ __forceinline__ void normalise_from_words(const XgEnd &e, int tid, in
 //   - V goes through registers (plain loads, stored to LDS at the end of the
 //     chunk), so no direct-to-LDS load is outstanding when the compiler
 //     waits for a fragment;
-//   - P^T fragments of key blocks a query tile does not reach are not loaded.
+//   - P^T fragments of key blocks a query tile does not reach are not loaded;
+//   - with 8 or more slices per pair, the S waves prefetch the pair's
+//     fragment lines of the chunk three ahead into L2, each slice its share.
 //
 // GroupNorm exchange (XG, 2 <= NS <= 8 slices per row).  The NS workgroups
 // of a (pair, segment) run through the same chunks side by side, so instead
@@ -1258,6 +1260,31 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                     *reinterpret_cast<bf16x4 *>(St + col * C::SP + row) = v4;
                 }
         };
+        // L2 prefetch of the pair's fragments PD chunks ahead.  All NS slices
+        // of a pair read every fragment line; without the prefetch the first
+        // reads of a line miss L2, and loads return in order, so each miss
+        // holds back the hits issued after it.  Slice s touches only its
+        // 1/NS share of a chunk's lines, one dword per 128-byte line, so the
+        // prefetch costs 1/NS extra requests per line: a gain at NS = 8 (the
+        // 7B-shaped layer: 299 -> 281 us), a loss at NS = 4 (long sequence),
+        // hence only from 8 slices.  The dword is kept live by an empty asm
+        // a chunk later, so the compiler's in-order load counts stay exact.
+        constexpr int PD = 3;
+        constexpr int QFB = C::NKT * C::KS * FRAG * 2, KFB = C::RT * C::NB * FRAG * 2, PFB = C::NKT * C::NB * FRAG * 2;
+        constexpr int NL = (QFB + KFB + PFB) / 128;  // fragment lines per chunk
+        const int lps = (NL + a.NS - 1) / a.NS;     // ... per slice
+        const int pl = slice * lps + w * 64 + lane;  // this lane's line
+        const bool pf_on = a.NS >= 8 && w * 64 + lane < lps && pl < NL;
+        uint32_t pfv = 0u;
+        auto prefetch = [&](int cj) {
+            cj = cj < nch ? cj : nch - 1;
+            const char *p = pl < QFB / 128   ? reinterpret_cast<const char *>(qfb) + (size_t)cj * QFB + pl * 128
+                            : pl < (QFB + KFB) / 128
+                                ? reinterpret_cast<const char *>(kfb) + (size_t)cj * KFB + (pl - QFB / 128) * 128
+                                : reinterpret_cast<const char *>(pfb) + (size_t)cj * PFB + (pl - (QFB + KFB) / 128) * 128;
+            asm volatile("" ::"v"(pfv));
+            if (pf_on) pfv = *reinterpret_cast<const uint32_t *>(p);
+        };
         write_st(St0);
         if (i1 > i0) {
             load_v(i0);
@@ -1268,6 +1295,9 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         auto chunk = [&](int ci, const char *Vc, char *Vn, __bf16 *Sn) {
             __syncthreads();
             load_v(ci + 1);
+            sched_fence();
+            prefetch(ci + PD);
+            sched_fence();
             {
                 const int j = ci % period;
                 if (j == 0) {
@@ -1307,6 +1337,7 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
             chunk(ci, Vb0, Vb1, St1);
             if (ci + 1 < i1) chunk(ci + 1, Vb1, Vb0, St0);
         }
+        asm volatile("" ::"v"(pfv));
         if (a.s_out && seg == a.nseg - 1) {
             const float f = exp2f((float)(BC * ph) * lg);
 #pragma unroll
