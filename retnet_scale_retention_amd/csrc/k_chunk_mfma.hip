@@ -1063,7 +1063,7 @@ __device__ __forceinline__ void normalise_from_words(const XgEnd &e, int tid, in
 //     waits for a fragment;
 //   - P^T fragments of key blocks a query tile does not reach are not loaded;
 //   - with 8 or more slices per pair, the S waves prefetch the pair's
-//     fragment lines of the chunk three ahead into L2, each slice its share.
+//     fragment lines of the next chunk into L2, each slice its share.
 //
 // GroupNorm exchange (XG, 2 <= NS <= 8 slices per row).  The NS workgroups
 // of a (pair, segment) run through the same chunks side by side, so instead
@@ -1269,7 +1269,11 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
         // 7B-shaped layer: 299 -> 281 us), a loss at NS = 4 (long sequence),
         // hence only from 8 slices.  The dword is kept live by an empty asm
         // a chunk later, so the compiler's in-order load counts stay exact.
-        constexpr int PD = 3;
+        // One chunk ahead is far enough: at two or three, part of the
+        // prefetched lines leave L2 before the slices read them and come in
+        // twice (7B-shaped call: 621 MB fetched at one chunk ahead, 636 MB at
+        // two, 893 MB at three; kernel time the same within the noise).
+        constexpr int PD = 1;
         constexpr int QFB = C::NKT * C::KS * FRAG * 2, KFB = C::RT * C::NB * FRAG * 2, PFB = C::NKT * C::NB * FRAG * 2;
         constexpr int NL = (QFB + KFB + PFB) / 128;  // fragment lines per chunk
         const int lps = (NL + a.NS - 1) / a.NS;     // ... per slice
