@@ -29,10 +29,13 @@ already resident in HBM.  The same JSON line also reports
   - long_sequence: the chunkwise forward over B=1, T=131072, H=8, d_k=128,
     d_v=256 at chunk 64, 128 and 256 (state carried across all chunks);
   - cpu_baseline: the fp64 oracle's chunkwise form timed on a bounded sample
-    of the same workload on the host cores (a reported baseline only).
+    of the same workload on the host cores (a reported baseline only);
+  - achievable_peaks: a 1 GiB device copy and a bf16 8192^3 matrix product
+    through torch, the rates plain work reaches here beside the published
+    peaks.
 Inputs are synthetic and seeded.  Usage:
   python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-parallel] [--no-backward]
-                  [--no-qkv] [--no-long] [--no-small] [--copy-mib N]
+                  [--no-qkv] [--no-long] [--no-small] [--no-peaks] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -94,6 +97,38 @@ def chunk_kernel_flops(T, H, B, dk, dv, b):
     """Algorithmic flops of the chunk-recurrence kernel: inter-chunk term and
     state update (2 d_k d_v each) plus the causal value product (b+1) d_v."""
     return B * T * H * (4 * dk * dv + (b + 1) * dv)
+
+
+def chunk_dense_flops(T, H, B, dk, dv, b):
+    """Flops the chunk tiles execute when every intra-chunk product is taken
+    over the full b x b block (the causal half included): 2 b (d_k + d_v) +
+    4 d_k d_v per token-head."""
+    return B * T * H * (2 * b * (dk + dv) + 4 * dk * dv)
+
+
+def achievable_peaks(torch):
+    """Rates this GPU reaches on plain work, as a second scale beside the
+    published peaks: a 1 GiB device copy (read + write bytes per second) and
+    a large bf16 matrix product through torch (hipBLASLt), 8192^3, both
+    operands contiguous.  Median of 10 reps each after 3 warm-ups."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    cp = per_call_ms(torch, lambda: dst.copy_(src), 10)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    mm = per_call_ms(torch, lambda: torch.mm(a, b, out=c), 10)
+    del a, b, c
+    copy_gbs = 2 * (1 << 30) / (float(np.median(cp)) / 1e3) / 1e9
+    gemm_tflops = 2 * n ** 3 / (float(np.median(mm)) / 1e3) / 1e12
+    return {"note": "1 GiB device copy (read + write) and a bf16 8192^3 torch.mm (hipBLASLt); medians of 10 reps",
+            "copy_GBs": copy_gbs, "copy_frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+            "gemm_tflops": gemm_tflops, "gemm_frac_of_peak": gemm_tflops / MFMA_BF16_PEAK_TFLOPS}
 
 
 def chunk_bytes(T, H, B, dk, dv):
@@ -267,10 +302,11 @@ def bench_chunkwise(torch, msr, mi, steps, warmup, chunk):
     del wsf
     kms = float(np.mean(kern_ms))
     flops = chunk_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
+    dflops = chunk_dense_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     kflops = chunk_kernel_flops(w.T, w.H, w.B, w.dk, w.dv, chunk)
     return {
         "workload": w, "chunk": chunk, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
-        "kernel_ms": kms, "flops": flops, "kernel_flops": kflops, "split_scores_ms": split_ms,
+        "kernel_ms": kms, "flops": flops, "dense_flops": dflops, "kernel_flops": kflops, "split_scores_ms": split_ms,
         "other_chunk": {"chunk": ochunk, "ms_per_step": other_ms, "tokens_per_s": w.B * w.T / (other_ms / 1e3),
                         "step_tflops": chunk_flops(w.T, w.H, w.B, w.dk, w.dv, ochunk) / (other_ms / 1e3) / 1e12},
         "bytes": chunk_bytes(w.T, w.H, w.B, w.dk, w.dv),
@@ -607,6 +643,7 @@ def main():
     ap.add_argument("--no-parallel", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -636,6 +673,7 @@ def main():
         bwd = {"small": bench_backward(torch, msr, mi, "small", 3, 64),
                "7b": bench_backward(torch, msr, mi, "7b", 5, 128)}
     qkv = None if args.no_qkv else bench_qkv(torch, msr, mi, 5, args.chunk)
+    peaks = None if args.no_peaks else achievable_peaks(torch)
     cpu = None if args.no_cpu else cpu_baseline(mi, args.chunk)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda:0")
@@ -675,7 +713,12 @@ def main():
             "achieved": r["flops"] / (r["call"]["median_ms"] / 1e3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": r["flops"] / (r["call"]["median_ms"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "flops_per_call": r["flops"], "algorithmic_bytes": r["bytes"],
-            "traffic": call_traffic_record(r["chunk"])},
+            "traffic": call_traffic_record(r["chunk"]),
+            "dense_chunk": {"note": "flops the full b x b intra-chunk tiles execute, 2b(dk+dv) + 4 dk dv per "
+                                    "token-head, over the same call time",
+                            "flops_per_call": r["dense_flops"],
+                            "tflops": r["dense_flops"] / (r["call"]["median_ms"] / 1e3) / 1e12}},
+        "achievable_peaks": peaks,
         "timing": {"call": r["call"], "kernel": r["kernel"], "flushed_call": r["flushed"]},
         "small_layer": sml,
         "split_scores": {"note": "the same call with MSR_FLAG_SPLIT_SCORES (precision option for strong decay)",

@@ -682,20 +682,10 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
                     S[rt][ct][r] = x;
                 }
         if (!SO) {
-            // earlier segments' end states, one whole tile set per segment
-            // (the loads of a segment are independent, so they overlap)
-            for (int gg = 0; gg < seg; ++gg) {
-                const float *e = a.segE + ebase + (size_t)gg * DK * c.dv;
-#pragma unroll
-                for (int rt = 0; rt < C::RPW; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                            S[rt][ct][r] = S[rt][ct][r] * gseg + e[(size_t)row * c.dv + col];
-                        }
-            }
+            // earlier segments' end states
+            fold_segments<64>(S, a.segE + ebase, (size_t)DK * c.dv, seg, gseg, [&](int rt, int ct, int r) {
+                return (size_t)((rbase + rt) * 16 + 4 * g + r) * c.dv + (cbase + ct) * 16 + l16;
+            });
 #pragma unroll
             for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll
@@ -1230,19 +1220,10 @@ __global__ __launch_bounds__((2 * Cfg<DK, BC>::THREADS)) void chunk_ws_kernel(Ms
                         const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
                         S[rt][ct][r] = sin_p ? sin_p[(size_t)row * c.dv + col] : 0.f;
                     }
-            // earlier segments' end states, one whole tile set per segment
-            for (int gg = 0; gg < seg; ++gg) {
-                const float *e = a.segE + ebase + (size_t)gg * DK * c.dv;
-#pragma unroll
-                for (int rt = 0; rt < C::RPW; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < C::CPW; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = (rbase + rt) * 16 + 4 * g + r, col = (cbase + ct) * 16 + l16;
-                            S[rt][ct][r] = S[rt][ct][r] * gseg + e[(size_t)row * c.dv + col];
-                        }
-            }
+            // earlier segments' end states
+            fold_segments<64>(S, a.segE + ebase, (size_t)DK * c.dv, seg, gseg, [&](int rt, int ct, int r) {
+                return (size_t)((rbase + rt) * 16 + 4 * g + r) * c.dv + (cbase + ct) * 16 + l16;
+            });
 #pragma unroll
             for (int rt = 0; rt < C::RPW; ++rt)
 #pragma unroll

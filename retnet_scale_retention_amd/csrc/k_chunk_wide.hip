@@ -363,17 +363,10 @@ __global__ __launch_bounds__(NWV * 64) void chunk_wide_kernel(MsrConst c, ChunkA
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[rt][ct][r] = has_in ? sin[sidx(rt, ct, r)] : 0.f;
-        if (!SO) {
-            for (int gg = 0; gg < seg; ++gg) {
-                const float *e = a.segE + ebase + gg * estride;
-#pragma unroll
-                for (int rt = 0; rt < C::RT; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) S[rt][ct][r] = S[rt][ct][r] * gseg + e[sidx(rt, ct, r)];
-            }
-        }
+        // earlier segments' end states (the prologue runs before the chunk
+        // loop's fragments and output tiles are live, so a batch of loads may
+        // take up to 128 registers)
+        if (!SO) fold_segments<128>(S, a.segE + ebase, estride, seg, gseg, sidx);
 #pragma unroll
         for (int rt = 0; rt < C::RT; ++rt)
 #pragma unroll

@@ -94,4 +94,53 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
     return s;
 }
 
+// ---- segmented chunk recurrence -------------------------------------------
+// Folds the end states E_0 .. E_(seg-1) of a pair's earlier segments into
+// the state tiles (4-float vectors V4) a lane holds, in segment order: S <- S gseg + E_g.  The
+// loads do not depend on S, so SB segments' tiles are loaded together and
+// folded afterwards: one memory round trip per SB segments instead of one
+// per segment (SB sized so the batch takes at most REGS registers).
+// off(rt, ct, r) is the element's offset within a segment's state, estride
+// the distance between segments.
+template <int REGS, int RPW, int CPW, class V4, class Off>
+__device__ __forceinline__ void fold_segments(V4 (&S)[RPW][CPW], const float *e0, size_t estride, int seg,
+                                              float gseg, Off off) {
+    constexpr int SB = 4 * RPW * CPW >= REGS ? 1 : REGS / (4 * RPW * CPW);
+    if constexpr (SB == 1) {
+        // no room for a staged batch: each load feeds its own fold
+        for (int gg = 0; gg < seg; ++gg) {
+            const float *e = e0 + (size_t)gg * estride;
+#pragma unroll
+            for (int rt = 0; rt < RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CPW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[rt][ct][r] = S[rt][ct][r] * gseg + e[off(rt, ct, r)];
+        }
+        return;
+    }
+    for (int g0 = 0; g0 < seg; g0 += SB) {
+        V4 ev[SB][RPW][CPW];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            // past the last segment: a repeat of it, loaded but not folded
+            const float *e = e0 + (size_t)(g0 + u < seg ? g0 + u : seg - 1) * estride;
+#pragma unroll
+            for (int rt = 0; rt < RPW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CPW; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ev[u][rt][ct][r] = e[off(rt, ct, r)];
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            if (g0 + u < seg) {
+#pragma unroll
+                for (int rt = 0; rt < RPW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CPW; ++ct) S[rt][ct] = S[rt][ct] * gseg + ev[u][rt][ct];
+            }
+    }
+}
+
 }  // namespace msr
