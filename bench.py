@@ -682,9 +682,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    # the chunk recurrence runs as the wide-slice kernel at b = 64, the
-    # warp-specialised kernel at b = 128 and the single-role kernel at b = 256
-    main_kernel = {64: "chunk_wide_kernel", 128: "chunk_ws_kernel"}.get(args.chunk, "chunk_mfma_kernel")
+    # the 7B-shaped layer's chunk recurrence runs as the warp-specialised
+    # kernel at b = 64 and 128 and as the single-role kernel at b = 256
+    main_kernel = "chunk_ws_kernel" if args.chunk <= 128 else "chunk_mfma_kernel"
     traffic = traffic_record(main_kernel)
     line = {
         "metric": "chunkwise MSR fwd tokens/s + decode steps/s; % of bf16 MFMA / HBM peak",

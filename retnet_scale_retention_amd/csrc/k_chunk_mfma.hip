@@ -2155,14 +2155,17 @@ MfmaPlan mfma_plan(const msr_problem *p, int chunk, bool split = false) {
     m.pf = m.kf + up(tokens * p->dk * 2);
     // (b/16) x (b/32) fragments of 1 KiB per chunk: b * 2 bytes per token-head
     m.stats = m.pf + up(tokens * chunk * 2);
-    // The wide-slice kernel at b = 64, where it is the faster one even with
-    // its state-only segment pass (7B-shaped layer: 0.53 against about
-    // 0.73 ms per call), and at b = 128 when it needs no segments (one
-    // workgroup per (pair, 256 columns) already fills the GPU): its full
-    // pass is faster than the warp-specialised kernel's (253 against 303 us
-    // at the 7B shape), but not by the 89 us its segment pass costs there.
+    // The wide-slice kernel when it needs no segments (one workgroup per
+    // (pair, 256 columns) already fills the GPU: the decode prefill at
+    // B = 64, 4.0 against 4.7 ms), and at b = 64 also when the 64-column
+    // kernels would need segments too (the long sequence: 1.02 against
+    // 1.04 ms).  Where the 64-column kernels fill the GPU without segments
+    // and the wide one would not, they win: at the 7B-shaped layer 0.37
+    // against 0.49 ms per call at b = 64, and at b = 128 the wide kernel's
+    // faster full pass (253 against 303 us) does not pay for its 89 us
+    // segment pass.
     const bool wide_ok = chunk_wide_supported(p->dk, p->dv, chunk) && !(p->flags & kFlagNoWide);
-    m.wide = wide_ok && (chunk == 64 || choose_nseg(p, chunk, 256) == 1);
+    m.wide = wide_ok && (choose_nseg(p, chunk, 256) == 1 || (chunk == 64 && choose_nseg(p, chunk, W) > 1));
     m.NS = p->dv / (m.wide ? 32 : W);  // GroupNorm partials per row
     // the warp-specialised kernel (b <= 128) normalises the rows itself when
     // they span 2 to 8 of its slices, exchanging slice statistics

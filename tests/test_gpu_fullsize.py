@@ -72,7 +72,7 @@ def run_chunkwise_like_bench(w, q, k, v, g, chunk, flags=0):
 FUSED = 16  # MSR_FLAG_FUSED: the fused schedule of the chunkwise form
 
 
-@pytest.mark.parametrize("chunk,flags", [(128, 0), (256, 0), (128, FUSED)])
+@pytest.mark.parametrize("chunk,flags", [(128, 0), (64, 0), (256, 0), (128, FUSED)])
 def test_7b_sampled_pairs_vs_oracle(seven_b, chunk, flags):
     w, q, k, v, g, ref = seven_b
     note(f"7B chunk {chunk} flags {flags}: gpu")
