@@ -655,6 +655,28 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
         for (int u = 0; u < C::NQT; ++u)
             pr[u][kb % C::R] = ldfrag(pfb, (size_t)(ci * C::NKT + qt[u]) * C::NB + kb);
     };
+    // L2 prefetch of the pair's fragment lines of the next chunk, each slice
+    // its 1/NS share, one dword per 128-byte line, in the full pass with 8 or
+    // more slices per pair (as in chunk_ws_kernel; 7B-shaped layer at b = 256:
+    // 0.581 -> 0.566 ms per call).  It is issued right after the chunk's
+    // barrier, before the chunk's V loads, so the fixed wait counts after
+    // the V loads are unchanged; the dword is kept live until the next
+    // prefetch, a chunk later.
+    constexpr int QFB = C::NKT * C::KS * FRAG * 2, KFB = C::RT * C::NB * FRAG * 2, PFB = C::NKT * C::NB * FRAG * 2;
+    constexpr int NL = (QFB + KFB + PFB) / 128;  // fragment lines per chunk
+    const int lps = (NL + a.NS - 1) / a.NS;     // ... per slice
+    const int pl = slice * lps + w * 64 + lane;  // this lane's line
+    const bool pf_on = !SO && a.NS >= 8 && w * 64 + lane < lps && pl < NL;
+    uint32_t pfv = 0u;
+    auto prefetch = [&](int cj) {
+        cj = cj < nch ? cj : nch - 1;
+        const char *p = pl < QFB / 128   ? reinterpret_cast<const char *>(qfb) + (size_t)cj * QFB + pl * 128
+                        : pl < (QFB + KFB) / 128
+                            ? reinterpret_cast<const char *>(kfb) + (size_t)cj * KFB + (pl - QFB / 128) * 128
+                            : reinterpret_cast<const char *>(pfb) + (size_t)cj * PFB + (pl - (QFB + KFB) / 128) * 128;
+        asm volatile("" ::"v"(pfv));
+        if (pf_on) pfv = *reinterpret_cast<const uint32_t *>(p);
+    };
 
     // ---- state tiles: d_k rows (rbase + rt) 16 + 4 g + r, columns (cbase + ct) 16 + l16
     f32x4 S[C::RPW][C::CPW];
@@ -766,6 +788,11 @@ __global__ __launch_bounds__((Cfg<DK, BC>::THREADS)) void chunk_mfma_kernel(MsrC
             wait_vm<C::VWAIT>();
         __syncthreads();
         if (SO) dma_v(ci + 1, Vn);
+        if constexpr (!SO) {
+            vmem_fence();
+            prefetch(ci + 1);
+            vmem_fence();
+        }
 
         // ---- O^T = (S_old^T Q~^T) xi.  After the MFMAs of k-step ks, memory
         // operation ks of [previous outputs of tile 0..NQT-1, next V units]
