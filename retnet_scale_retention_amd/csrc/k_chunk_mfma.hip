@@ -1069,9 +1069,11 @@ __device__ __forceinline__ void normalise_from_words(const XgEnd &e, int tid, in
 // "S" waves run the state update and the V loads with the state tiles of
 // wave w - 4.  Both kinds meet at one barrier per chunk; the S waves write
 // S_new^T for the next chunk's inter-chunk product into the other LDS
-// buffer.  The kernel is bound by the vector-memory requests each CU can
-// keep in flight (the fragments of a pair are read by all of its value
-// slices), so:
+// buffer.  The kernel waits on memory most of the time (the fragments of a
+// pair are read by all of its value slices, from L2, and V and O stream
+// through HBM; at the 7B shape a call at B = 1 on half the CUs runs each
+// workgroup twice as fast, so the shared L2-miss path, not the CU, sets the
+// pace), so:
 //   - each fragment load is issued right after the last use of its
 //     registers, a chunk ahead of its next use (full scheduling barriers
 //     keep the compiler from sinking the loads to the end of the chunk);

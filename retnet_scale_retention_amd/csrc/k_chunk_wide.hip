@@ -7,8 +7,8 @@
 // over the fragments prep_kernel writes (QF in its QPERM order, KF, PF), but a
 // workgroup owns 256 value columns instead of 64.  Every value slice needs
 // all of its chunk's QF, KF and PF fragments; with 64-column slices the chunk
-// kernels fetch them from L2 once per 64 columns and are bound by the
-// requests a CU keeps in flight.  Here one fetch into LDS serves 256 columns.
+// kernels fetch them from L2 once per 64 columns.  Here one fetch into LDS
+// serves 256 columns.
 //
 // Workgroup: 8 waves, two per SIMD, owning (pair, 256 value columns, segment
 // of chunks).  Wave w owns columns 32 w .. 32 w + 31 of the slice and keeps
