@@ -326,6 +326,10 @@ XG_CASES = [  # (B, T, H, dk, dv, chunk)
     # 64 pairs x 8 slices: more workgroups than the GPU holds at once, so the
     # rows take the separate GroupNorm pass instead of the exchange
     (4, 256, 16, 64, 512, 128),
+    # b = 64 shapes the wide-slice kernel also takes but would need segments
+    # for: they run on this kernel (256 workgroups, no segments)
+    (4, 256, 16, 128, 256, 64),
+    (2, 256, 16, 256, 512, 64),
 ]
 
 
