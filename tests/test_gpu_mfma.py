@@ -21,6 +21,11 @@ CASES = [  # (B, T, H, dk, dv, chunk)
     (1, 192, 2, 256, 64, 64),
     (1, 512, 1, 256, 128, 256),
     (1, 384, 2, 256, 192, 128),
+    # b = 256 with 8 value slices per pair: the full pass prefetches the next
+    # chunk's fragment lines into L2 (also with segments)
+    (1, 512, 2, 128, 512, 256),
+    (1, 2048, 1, 128, 512, 256),
+    (1, 512, 1, 256, 512, 256),
 ]
 
 
